@@ -1,0 +1,44 @@
+"""The seeded generator: deterministic, right shapes, dtypes and distributions,
+and scores that keep exp inside fp16 range (the graph has no max subtraction,
+so the generated inputs must keep exp(QK) finite in fp16: max score < ln 65504)."""
+import math
+
+import numpy as np
+import pytest
+
+from gqa_attention_split_amd.inputs import CONFIGS, CONFIG_ORDER, make_config, make_qkv
+
+
+def test_same_seed_same_bytes_and_new_seed_new_bytes():
+    a = make_qkv(2, 16, 64, seed=9)
+    b = make_qkv(2, 16, 64, seed=9)
+    c = make_qkv(2, 16, 64, seed=10)
+    for x, y in zip(a, b):
+        assert x.tobytes() == y.tobytes()
+    assert a[0].tobytes() != c[0].tobytes()
+
+
+@pytest.mark.parametrize("name", [n for n in CONFIG_ORDER if CONFIGS[n].B * CONFIGS[n].N <= 2**20])
+def test_config_shapes_dtypes_and_distributions(name):
+    cfg = CONFIGS[name]
+    q, k, v = make_config(cfg)
+    assert q.shape == (cfg.B, cfg.M, 64) and k.shape == (cfg.B, 64, cfg.N)
+    assert v.shape == (cfg.B, cfg.N, 64)
+    for x in (q, k, v):
+        assert x.dtype == np.float16 and x.flags["C_CONTIGUOUS"]
+    assert abs(float(q.astype(np.float64).std()) - cfg.qk_std) < 0.02 * cfg.qk_std + 1e-3
+    assert abs(float(k.astype(np.float64).std()) - cfg.qk_std) < 0.02 * cfg.qk_std + 1e-3
+    vs = v.astype(np.float64)
+    if cfg.v_dist == "normal":
+        assert abs(vs.std() - 1.0) < 0.02
+    else:
+        assert vs.min() >= -1.0 and vs.max() <= 1.0 and abs(vs.std() - 1 / math.sqrt(3)) < 0.02
+    # Scores stay far below the fp16 overflow point of exp.
+    scores = np.matmul(q.astype(np.float32), k.astype(np.float32))
+    assert float(scores.max()) < math.log(65504.0) - 4.0
+
+
+def test_work_and_bytes_formulas():
+    cfg = CONFIGS["gqa_b16_m256_n4096"]
+    assert cfg.flops == 4 * 16 * 256 * 4096 * 64
+    assert cfg.algorithmic_bytes == 256 * 16 * (256 + 4096)
