@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the fused GQA exp-sum-div path on one MI355X.
+
+One step = one mga_gqa_forward call (split-KV partial kernel + combine kernel)
+over one batch of synthetic input: Q (16, 256, 64), K (16, 64, 4096),
+V (16, 4096, 64) fp16 by default (the tutorial graph at batch 8). Inputs sit
+in HBM before timing starts. The timed steps cycle through R copies of the
+inputs totalling at least --rotate-bytes (default 1 GiB), so that no step finds
+its K/V in the 256 MB Infinity Cache; a same-buffer ("hot") figure is reported
+beside it.
+
+Timing follows the profiling protocol on the Mirage pages (16 warm-up
+iterations, then many timed iterations between two events, mean per
+iteration): the steps are captured once in a HIP graph and replayed, so the
+host's launch rate does not limit the measurement; events sit on the stream
+the kernels run on. The partial kernel (the dominant one) is timed alone the
+same way for the roofline entry.
+
+Prints ONE JSON line. --gpus above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_FP16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gqa_partial_b16_m256_n4096.md")
+KERNEL_SRC = os.path.join(ROOT, "gqa_attention_split_amd", "csrc", "gqa_kernels.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="gqa_b16_m256_n4096")
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's policy")
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--graph-steps", type=int, default=200, help="steps captured per HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU work for the oracle baseline sample")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="also run one plain device-to-device copy of known size "
+                         "(reference dispatch for FETCH_SIZE / WRITE_SIZE scaling)")
+    ap.add_argument("--eager", action="store_true", help="also time without graphs")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(config: str):
+    """Counter-derived HBM bytes per partial-kernel launch, if the committed
+    counter summary was taken on the current kernel source; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    cfg = re.search(r"workload:\s*(\S+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (sha and cfg and val) or sha.group(1) != kernel_source_sha() or cfg.group(1) != config:
+        return None
+    return float(val.group(1))
+
+
+def time_graph(torch, stream, fn, n_steps, graph_steps, warmup):
+    """Capture `graph_steps` calls of fn(i) in one graph, replay to cover n_steps,
+    return mean ms per call (events on `stream`)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(graph_steps):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(n_steps / graph_steps))
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / (reps * graph_steps), reps * graph_steps
+
+
+def time_eager(torch, stream, fn, n_steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(n_steps):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n_steps
+
+
+def cpu_baseline(cfg, q, k, v, target_s):
+    """The oracle as it stands, on the host's cores, on whole query rows of the
+    same workload (a row costs the same at any row index)."""
+    import numpy as np
+
+    import oracle
+    rows_per_b = cfg.M
+    # Probe one batch row's slice to size the sample.
+    probe_rows = min(cfg.M, 8)
+    t0 = time.perf_counter()
+    oracle.gqa_f64(np.ascontiguousarray(q[:1, :probe_rows]), k[:1], v[:1])
+    per_row = max((time.perf_counter() - t0) / probe_rows, 1e-9)
+    total_rows = cfg.B * rows_per_b
+    want_rows = int(min(total_rows, max(1, target_s / per_row)))
+    nb = max(1, min(cfg.B, want_rows // rows_per_b))
+    m = rows_per_b if want_rows >= rows_per_b else max(1, want_rows)
+    qs = np.ascontiguousarray(q[:nb, :m])
+    t0 = time.perf_counter()
+    oracle.gqa_f64(qs, k[:nb], v[:nb])
+    dt = time.perf_counter() - t0
+    flops = 4 * nb * m * cfg.N * cfg.D
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": (f"{nb} of {cfg.B} batch rows x {m} of {cfg.M} query rows x all {cfg.N} keys "
+                   f"({flops / 1e9:.2f} GFLOP, {dt:.2f} s, fp64 C loops, OpenMP)"),
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build measures one GPU only (asked for {max(args.gpus, world)}); "
+              "the fused GQA path shards over the batch axis with no exchange, but no "
+              "multi-GPU run is part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gqa_attention_split_amd as mga
+    from gqa_attention_split_amd.inputs import CONFIGS, make_config
+
+    cfg = CONFIGS[args.config]
+    B, M, N = cfg.B, cfg.M, cfg.N
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+
+    q, k, v = make_config(cfg)
+    set_bytes = q.nbytes + k.nbytes + v.nbytes + B * M * 64 * 2
+    R = max(1, min(1024, math.ceil(args.rotate_bytes / set_bytes)))
+    base = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
+    outs = [torch.empty((B, M, 64), dtype=torch.float16, device=dev) for _ in range(R)]
+    splits = args.splits if args.splits > 0 else mga.mga_gqa_choose_splits(B, M, N)
+    eff = mga.mga_gqa_effective_splits(B, M, N, splits)
+    ws = mga.workspace_for(B, M, N, splits, device=dev)
+    ws_ptr = 0 if ws is None else ws.data_ptr()
+    ws_bytes = 0 if ws is None else ws.numel()
+    lib = mga._lib.load()
+    sh = stream.cuda_stream
+    ptrs = [tuple(t.data_ptr() for t in s) for s in sets]
+    optr = [o.data_ptr() for o in outs]
+    torch.cuda.synchronize()
+
+    def fwd(i, rotate=True):
+        j = i % R if rotate else 0
+        rc = lib.mga_gqa_forward(*ptrs[j], optr[j], B, M, N, splits, ws_ptr, ws_bytes, sh)
+        if rc:
+            raise mga.GqaError(rc)
+
+    def partial(i, rotate=True):
+        j = i % R if rotate else 0
+        rc = lib.mga_gqa_partial(*ptrs[j], optr[j], B, M, N, splits, ws_ptr, ws_bytes, sh)
+        if rc:
+            raise mga.GqaError(rc)
+
+    print(f"[bench] {cfg.name} B={B} M={M} N={N} splits={eff} rotating sets={R} "
+          f"({R * set_bytes / 2**20:.0f} MiB) steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    gsteps = max(1, min(args.graph_steps, args.steps))
+    with torch.cuda.stream(stream):
+        ms_step, timed = time_graph(torch, stream, fwd, args.steps, gsteps, args.warmup)
+        print(f"[bench] forward {ms_step * 1e3:.3f} us/step", file=sys.stderr, flush=True)
+        ms_partial, _ = time_graph(torch, stream, partial, args.steps, gsteps, args.warmup)
+        print(f"[bench] partial kernel {ms_partial * 1e3:.3f} us/launch", file=sys.stderr, flush=True)
+        ms_hot, _ = time_graph(torch, stream, lambda i: fwd(i, rotate=False), args.steps, gsteps,
+                               args.warmup)
+        ms_eager = time_eager(torch, stream, fwd, args.steps, args.warmup) if args.eager else None
+        if args.pmc_calibrate:
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+    torch.cuda.synchronize()
+
+    flops = cfg.flops
+    alg_bytes = cfg.algorithmic_bytes
+    s = ms_step * 1e-3
+    tflops = flops / s / 1e12
+    gbps = alg_bytes / s / 1e9
+    t_mfma = flops / (MFMA_FP16_PEAK_TFLOPS * 1e12)
+    t_hbm = alg_bytes / (HBM_PEAK_GBPS * 1e9)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    sp = ms_partial * 1e-3
+    if bound == "hbm":
+        achieved, peak, unit = alg_bytes / sp / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        achieved, peak, unit = flops / sp / 1e12, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"
+
+    result = {
+        "metric": "fused GQA exp-sum-div attention TFLOP/s (+ HBM GB/s) on 1 MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": timed,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "M": M, "N": N, "D": cfg.D,
+                   "q_k_std": cfg.qk_std, "v_dist": cfg.v_dist, "seed": cfg.seed,
+                   "splits": eff, "rotating_sets": R, "timing": "hip-graph replay, events on the launch stream"},
+        "hbm_gbps": round(gbps, 1),
+        "frac_hbm_peak": round(t_hbm / s, 4),
+        "frac_mfma_peak": round(t_mfma / s, 4),
+        "hot_ms_per_step": round(ms_hot, 6),
+        "partial_kernel_ms": round(ms_partial, 6),
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": read_traffic(cfg.name),
+                     "kernel": "gqa_partial_kernel"},
+    }
+    if ms_eager is not None:
+        result["eager_ms_per_step"] = round(ms_eager, 6)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 6)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

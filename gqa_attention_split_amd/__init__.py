@@ -1,0 +1,140 @@
+"""Fused GQA exp-sum-div attention for MI355X (gfx950).
+
+Computes the Mirage GQA tutorial graph ("Mirage: Define GQA Computation
+Graph"): O = (E / rowsum(E)) V with E = exp(Q K), Q (B, M, 64), K stored
+head-dim-major as (B, 64, N), V (B, N, 64), all fp16, no scale and no max
+subtraction.
+
+The functions named ``mga_*`` mirror the C ABI in ``include/mga_gqa.h`` one to
+one and only marshal arguments (pointers may be ints or torch tensors; the
+stream may be an int handle or a torch stream). ``gqa_forward`` is the
+convenience form for torch tensors: it validates, allocates the output and
+the workspace with torch, and calls ``mga_gqa_forward``. Every step of the
+computation runs in the HIP kernels; nothing here computes.
+"""
+from __future__ import annotations
+
+from . import _lib
+
+MGA_OK = 0
+MGA_ERR_INVALID_VALUE = 1
+MGA_ERR_LAYOUT = 2
+MGA_ERR_CONFIG = 3
+MGA_ERR_WORKSPACE = 4
+MGA_ERR_HIP = 5
+KEY_BLOCK = 128
+HEAD_DIM = 64
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(mga_status_string(status))
+        self.status = status
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+# ------------------------------------------------------ C ABI, 1:1 ----
+def mga_status_string(status: int) -> str:
+    return _lib.load().mga_status_string(int(status)).decode()
+
+
+def mga_gqa_choose_splits(B: int, M: int, N: int) -> int:
+    return _lib.load().mga_gqa_choose_splits(B, M, N)
+
+
+def mga_gqa_effective_splits(B: int, M: int, N: int, splits: int) -> int:
+    return _lib.load().mga_gqa_effective_splits(B, M, N, splits)
+
+
+def mga_gqa_workspace_bytes(B: int, M: int, N: int, splits: int) -> int:
+    return _lib.load().mga_gqa_workspace_bytes(B, M, N, splits)
+
+
+def mga_gqa_check_args(q, k, v, o, B, M, N, splits, ws, ws_bytes) -> int:
+    return _lib.load().mga_gqa_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
+                                          _ptr(ws), ws_bytes)
+
+
+def mga_gqa_forward(q, k, v, o, B, M, N, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
+                                       _ptr(ws), ws_bytes, _stream(stream))
+
+
+def mga_gqa_partial(q, k, v, o, B, M, N, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
+                                       _ptr(ws), ws_bytes, _stream(stream))
+
+
+def mga_gqa_combine(o, B, M, N, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_combine(_ptr(o), B, M, N, splits, _ptr(ws), ws_bytes,
+                                       _stream(stream))
+
+
+# ------------------------------------------------- torch convenience ----
+def _check_tensors(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be 3-D")
+    B, M, D = q.shape
+    if D != HEAD_DIM:
+        raise ValueError(f"head dim must be {HEAD_DIM}, got {D}")
+    if k.shape[0] != B or k.shape[1] != D:
+        raise ValueError(f"k must be (B, 64, N) = ({B}, 64, N), got {tuple(k.shape)}")
+    N = k.shape[2]
+    if tuple(v.shape) != (B, N, D):
+        raise ValueError(f"v must be (B, N, 64) = ({B}, {N}, 64), got {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    return B, M, N
+
+
+def workspace_for(B: int, M: int, N: int, splits: int = 0, device=None):
+    """A torch uint8 workspace of mga_gqa_workspace_bytes(...) bytes (or None)."""
+    import torch
+    nbytes = mga_gqa_workspace_bytes(B, M, N, splits)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None):
+    """O = (exp(QK) / rowsum) V for fp16 CUDA tensors q (B,M,64), k (B,64,N), v (B,N,64)."""
+    import torch
+    B, M, N = _check_tensors(q, k, v)
+    if out is None:
+        out = torch.empty((B, M, HEAD_DIM), dtype=torch.float16, device=q.device)
+    elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, HEAD_DIM) or \
+            not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous float16 (B, M, 64) tensor on q's device")
+    need = mga_gqa_workspace_bytes(B, M, N, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = mga_gqa_forward(q, k, v, out, B, M, N, splits, workspace, ws_bytes, stream)
+    if rc != MGA_OK:
+        raise GqaError(rc)
+    return out

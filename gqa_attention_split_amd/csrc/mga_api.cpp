@@ -1,0 +1,165 @@
+// Host side of the C ABI: argument checks, split policy, workspace sizing and
+// the two launches. See include/mga_gqa.h for the contract of each entry point.
+//
+// The split count is a grid-dimension choice (the kaispace blog, section 4.2,
+// describes the grid and for-loop ranges as search parameters; here a fixed
+// rule picks them), and the workspace plays the role of the runtime buffer
+// whose size the CUDA transpiler reports (blog section 5.2) and that the
+// generated entry point receives as its `buf` argument (Mirage docs,
+// "Generated CUDA Code Example").
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <climits>
+
+#include "../../include/mga_gqa.h"
+#include "mga_internal.h"
+
+namespace mga {
+
+namespace {
+
+constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kTargetGroups = 2 * kCUs;
+constexpr int kMinBlocksPerSplit = 2;
+
+inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+int query_groups_for(int M) {
+    if (M > 128) return 4;
+    if (M > 64) return 2;
+    return 1;
+}
+
+// Policy: enough workgroups for two per compute unit, but at least two key
+// blocks per split so the double buffer has something to overlap.
+int policy_splits(int B, int M, int N) {
+    if (N < 1 || B < 1 || M < 1) return 1;
+    const long long nblocks = ceil_div(N, kKeyBlock);
+    const long long base = (long long)B * ceil_div(M, 64LL * query_groups_for(M));
+    long long s = ceil_div(kTargetGroups, base);
+    s = std::min(s, std::max(1LL, nblocks / kMinBlocksPerSplit));
+    return (int)std::max(1LL, s);
+}
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+}  // namespace
+
+int make_plan(int B, int M, int N, int splits, Plan *p) {
+    if (B < 0 || M < 0 || N < 1 || splits < 0) return MGA_ERR_INVALID_VALUE;
+    if (N % 8 != 0) return MGA_ERR_LAYOUT;
+    const long long nblocks = ceil_div(N, kKeyBlock);
+    if (splits > nblocks) return MGA_ERR_CONFIG;
+    p->B = B;
+    p->M = M;
+    p->N = N;
+    p->qgroups = query_groups_for(M);
+    p->tile_rows = 64 * p->qgroups;
+    p->mtiles = (int)ceil_div(M, p->tile_rows);
+    p->nblocks = (int)nblocks;
+    const int want = splits == 0 ? policy_splits(B, M, N) : splits;
+    const long long chunk_blocks = ceil_div(nblocks, want);
+    p->splits = (int)ceil_div(nblocks, chunk_blocks);
+    p->chunk_keys = (int)(chunk_blocks * kKeyBlock);
+    if (B > 65535 || p->mtiles > 65535) return MGA_ERR_CONFIG;
+    if (p->splits > 1) {
+        const size_t rows = (size_t)p->splits * B * M;
+        const size_t bytes = rows * kHeadDim * sizeof(float) + rows * sizeof(float);
+        p->ws_bytes = (bytes + 255) & ~(size_t)255;
+    } else {
+        p->ws_bytes = 0;
+    }
+    return MGA_OK;
+}
+
+int check_call(const void *q, const void *k, const void *v, const void *o, const Plan &p,
+               const void *ws, size_t ws_bytes, bool need_inputs) {
+    if (p.B == 0 || p.M == 0) return MGA_OK;
+    if (!o || (need_inputs && (!q || !k || !v))) return MGA_ERR_INVALID_VALUE;
+    if (misaligned(o) || (need_inputs && (misaligned(q) || misaligned(k) || misaligned(v))))
+        return MGA_ERR_LAYOUT;
+    if (p.ws_bytes > 0 && (!ws || misaligned(ws) || ws_bytes < p.ws_bytes))
+        return MGA_ERR_WORKSPACE;
+    return MGA_OK;
+}
+
+}  // namespace mga
+
+extern "C" {
+
+const char *mga_status_string(int status) {
+    switch (status) {
+    case MGA_OK: return "MGA_OK: success";
+    case MGA_ERR_INVALID_VALUE:
+        return "MGA_ERR_INVALID_VALUE: null pointer, negative B/M/splits, or N < 1";
+    case MGA_ERR_LAYOUT:
+        return "MGA_ERR_LAYOUT: pointer not 16-byte aligned or N not a multiple of 8";
+    case MGA_ERR_CONFIG:
+        return "MGA_ERR_CONFIG: splits above ceil(N/128) or grid dimension above 65535";
+    case MGA_ERR_WORKSPACE: return "MGA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MGA_ERR_HIP: return "MGA_ERR_HIP: kernel launch failed";
+    default: return "unknown mga status";
+    }
+}
+
+int mga_gqa_choose_splits(int B, int M, int N) {
+    mga::Plan p;
+    if (mga::make_plan(B, M, N, 0, &p) != MGA_OK) return 1;
+    return p.splits;
+}
+
+int mga_gqa_effective_splits(int B, int M, int N, int splits) {
+    mga::Plan p;
+    if (mga::make_plan(B, M, N, splits, &p) != MGA_OK) return -1;
+    return p.splits;
+}
+
+size_t mga_gqa_workspace_bytes(int B, int M, int N, int splits) {
+    mga::Plan p;
+    if (mga::make_plan(B, M, N, splits, &p) != MGA_OK) return 0;
+    return p.ws_bytes;
+}
+
+int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o, int B, int M,
+                       int N, int splits, const void *ws, size_t ws_bytes) {
+    mga::Plan p;
+    const int rc = mga::make_plan(B, M, N, splits, &p);
+    if (rc != MGA_OK) return rc;
+    return mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
+}
+
+int mga_gqa_partial(const void *q, const void *k, const void *v, void *o, int B, int M, int N,
+                    int splits, void *ws, size_t ws_bytes, void *stream) {
+    mga::Plan p;
+    int rc = mga::make_plan(B, M, N, splits, &p);
+    if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
+    if (rc != MGA_OK) return rc;
+    if (B == 0 || M == 0) return MGA_OK;
+    return mga::launch_partial(p, q, k, v, o, ws, stream) == 0 ? MGA_OK : MGA_ERR_HIP;
+}
+
+int mga_gqa_combine(void *o, int B, int M, int N, int splits, const void *ws, size_t ws_bytes,
+                    void *stream) {
+    mga::Plan p;
+    int rc = mga::make_plan(B, M, N, splits, &p);
+    if (rc == MGA_OK) rc = mga::check_call(nullptr, nullptr, nullptr, o, p, ws, ws_bytes, false);
+    if (rc != MGA_OK) return rc;
+    if (B == 0 || M == 0 || p.splits == 1) return MGA_OK;
+    return mga::launch_combine(p, o, ws, stream) == 0 ? MGA_OK : MGA_ERR_HIP;
+}
+
+int mga_gqa_forward(const void *q, const void *k, const void *v, void *o, int B, int M, int N,
+                    int splits, void *ws, size_t ws_bytes, void *stream) {
+    mga::Plan p;
+    int rc = mga::make_plan(B, M, N, splits, &p);
+    if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
+    if (rc != MGA_OK) return rc;
+    if (B == 0 || M == 0) return MGA_OK;
+    if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
+    if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
+    return MGA_OK;
+}
+
+}  // extern "C"

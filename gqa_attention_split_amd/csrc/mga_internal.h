@@ -1,0 +1,36 @@
+// Internal declarations shared by the host dispatch and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+
+namespace mga {
+
+// Geometry of one launch, decided on the host before anything is enqueued.
+struct Plan {
+    int B, M, N;
+    int qgroups;      // 16-row query groups per wave (1, 2 or 4); rows per workgroup = 64 * qgroups
+    int tile_rows;    // 64 * qgroups
+    int mtiles;       // ceil(M / tile_rows)
+    int nblocks;      // ceil(N / key block)
+    int splits;       // effective split count (>= 1)
+    int chunk_keys;   // keys per split (a multiple of the key block)
+    size_t ws_bytes;  // workspace the plan needs (0 when splits == 1)
+};
+
+constexpr int kKeyBlock = 128;
+constexpr int kHeadDim = 64;
+constexpr int kThreads = 256;
+
+// Fills `p` for a call; returns an mga_status (0 = ok). Host only, no HIP calls.
+int make_plan(int B, int M, int N, int splits, Plan *p);
+
+// Argument checks shared by every entry point (host only).
+int check_call(const void *q, const void *k, const void *v, const void *o, const Plan &p,
+               const void *ws, size_t ws_bytes, bool need_inputs);
+
+// Kernel launchers (gqa_kernels.hip). Return 0 or a hipError_t value.
+int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,
+                   void *ws, void *stream);
+int launch_combine(const Plan &p, void *o, const void *ws, void *stream);
+
+}  // namespace mga

@@ -1,0 +1,129 @@
+/*
+ * mga_gqa.h -- C ABI of the MI355X (gfx950) fused GQA exp-sum-div library.
+ *
+ * Operation (Mirage documentation, GQA tutorial, "Mirage: Define GQA
+ * Computation Graph"; the same graph is section 1 of the kaispace blog post
+ * on Mirage's muGraph search):
+ *
+ *     A = Q K,  E = exp(A),  S = rowsum(E) over the keys,  O = (E / S) V
+ *
+ * with no 1/sqrt(d) scale and no max subtraction. Per (b, i) row:
+ *     O[b,i,j] = sum_n exp(a_n) V[b,n,j] / sum_n exp(a_n),
+ *     a_n      = sum_d Q[b,i,d] K[b,d,n].
+ *
+ * The library evaluates it as split-KV partial sums plus a combine, the
+ * two-block-graph form that the blog's sections 2.1 and 4.2-4.3 describe for
+ * the "attention" search configuration (a for-loop over the key dimension with
+ * accumulation, then a combine across grid blocks). Because the graph
+ * subtracts no running maximum, partials combine by plain sums:
+ *     O = (sum_s W_s) / (sum_s L_s),  W_s = sum_{n in split s} e_n V[n],
+ *                                     L_s = sum_{n in split s} e_n.
+ *
+ * Data layout (all row-major, contiguous, IEEE fp16, device memory):
+ *     q [B][M][64]     query rows (axis 0 = batch x KV heads)
+ *     k [B][64][N]     keys stored head-dim-major ("pre-transposed")
+ *     v [B][N][64]     values
+ *     o [B][M][64]     output, written with round-to-nearest-even
+ * The head dimension is fixed at 64. Pointers must be 16-byte aligned and N a
+ * multiple of 8 (every K row then starts on a 16-byte boundary).
+ *
+ * Numerics: fp16 MFMA products with fp32 accumulation; exp in fp32 via the
+ * hardware exp2; P = fp16(E) feeds the second product, and the row-sum is
+ * taken from the same fp16 P (so numerator and denominator see identical
+ * weights). Results are deterministic for a fixed (shape, splits): the
+ * partials are combined in split order and no atomics are used. Inputs whose
+ * scores reach ln(65504) ~ 11.09 overflow fp16 P; results are then undefined
+ * (the graph itself overflows there).
+ *
+ * Ownership and asynchrony: the caller owns q, k, v, o and the workspace; the
+ * library allocates and frees nothing on the device and keeps no device state,
+ * so calls are reentrant. Work is enqueued on `stream` (a hipStream_t; NULL =
+ * the legacy default stream) with no host synchronisation; a fault inside a
+ * kernel surfaces at the caller's next synchronisation.
+ *
+ * Errors: every entry point validates its arguments on the host before any
+ * launch and returns an mga_status; on a nonzero status nothing was launched,
+ * except MGA_ERR_HIP, which reports a failed launch (hipGetLastError).
+ */
+#ifndef MGA_GQA_H
+#define MGA_GQA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. The numbering follows the transpiler error codes the kaispace
+ * blog lists in its section 5.1 (success 0, insufficient shared memory 1,
+ * layout error 2, config error 3), extended for this library. */
+typedef enum {
+    MGA_OK = 0,
+    MGA_ERR_INVALID_VALUE = 1, /* null pointer, B or M < 0, N < 1, splits < 0      */
+    MGA_ERR_LAYOUT = 2,        /* pointer not 16-byte aligned, or N % 8 != 0        */
+    MGA_ERR_CONFIG = 3,        /* splits > ceil(N / 128) or a grid dimension > 65535 */
+    MGA_ERR_WORKSPACE = 4,     /* workspace missing, misaligned or too small        */
+    MGA_ERR_HIP = 5            /* a kernel launch failed                            */
+} mga_status;
+
+/* Keys per pipeline stage; split chunks are whole multiples of it. */
+#define MGA_KEY_BLOCK 128
+/* Head dimension supported by this build. */
+#define MGA_HEAD_DIM 64
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *mga_status_string(int status);
+
+/* Split policy (host only, deterministic): the number of KV splits the
+ * library uses for this shape when the caller passes splits = 0. Always in
+ * [1, ceil(N / 128)]; returns 1 for N < 1. Following the kaispace blog
+ * (section 4.2), the split count is a grid-dimension choice; here a fixed
+ * rule picks it instead of a search. */
+int mga_gqa_choose_splits(int B, int M, int N);
+
+/* The split count actually launched for a requested `splits` (0 = policy):
+ * the chunk is ceil(ceil(N/128) / splits) key blocks and the count is
+ * ceil(ceil(N/128) / chunk), so that no split is empty. Returns -1 for
+ * arguments mga_gqa_check_args would reject with INVALID_VALUE or CONFIG. */
+int mga_gqa_effective_splits(int B, int M, int N, int splits);
+
+/* Bytes of workspace mga_gqa_forward needs: 0 when the effective split count
+ * is 1, else s*B*M*64*4 (fp32 numerators W[s][B][M][64]) + s*B*M*4 (fp32
+ * denominators L[s][B][M]), rounded up to 256. Returns 0 for invalid shapes. */
+size_t mga_gqa_workspace_bytes(int B, int M, int N, int splits);
+
+/* Host-only validation of a forward call; makes no HIP call and launches
+ * nothing, so it is usable without a GPU. Returns the status
+ * mga_gqa_forward would return before launching. `ws` may be NULL when the
+ * effective split count is 1. B == 0 or M == 0 is valid (a no-op). */
+int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o,
+                       int B, int M, int N, int splits, const void *ws, size_t ws_bytes);
+
+/* The whole path: partial kernel, then (when the effective split count is
+ * above 1) the combine kernel, both on `stream`. splits = 0 lets the policy
+ * choose. ws/ws_bytes: caller-owned device workspace of at least
+ * mga_gqa_workspace_bytes(B, M, N, splits) bytes, 16-byte aligned. */
+int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
+                    int B, int M, int N, int splits, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Only the split-KV partial kernel (the for-loop over keys). With one
+ * effective split it writes O directly (normalised, fp16); otherwise it
+ * writes the partial numerators and denominators into `ws` and leaves `o`
+ * untouched. Same arguments and checks as mga_gqa_forward. */
+int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
+                    int B, int M, int N, int splits, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Only the combine kernel: O[b,i,:] = fp16(sum_s W[s,b,i,:] / sum_s L[s,b,i])
+ * with the sums taken in split order. `ws` holds the partials a preceding
+ * mga_gqa_partial call wrote for the same (B, M, N, splits); q, k and v are
+ * not read. A no-op returning MGA_OK when the effective split count is 1. */
+int mga_gqa_combine(void *o, int B, int M, int N, int splits,
+                    const void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGA_GQA_H */

@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and its host-only entry points (status strings, split policy,
+workspace sizing, argument checks) behave as documented. No kernel runs."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import gqa_attention_split_amd as mga
+from gqa_attention_split_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mga_gqa.h")
+A = 1 << 20  # a 16-byte-aligned fake device address; check_args never dereferences
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mga_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert header_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+
+
+def test_status_strings():
+    for code in range(6):
+        s = mga.mga_status_string(code)
+        assert s.startswith("MGA_"), s
+    assert "unknown" in mga.mga_status_string(99)
+
+
+def _check(B=2, M=256, N=4096, splits=0, q=A, k=A, v=A, o=A, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = mga.mga_gqa_workspace_bytes(B, M, N, splits)
+    return mga.mga_gqa_check_args(q, k, v, o, B, M, N, splits, ws, ws_bytes)
+
+
+def test_check_args_codes():
+    assert _check() == mga.MGA_OK
+    assert _check(q=None) == mga.MGA_ERR_INVALID_VALUE
+    assert _check(o=None) == mga.MGA_ERR_INVALID_VALUE
+    assert _check(B=-1) == mga.MGA_ERR_INVALID_VALUE
+    assert _check(M=-1) == mga.MGA_ERR_INVALID_VALUE
+    assert _check(N=0) == mga.MGA_ERR_INVALID_VALUE
+    assert _check(splits=-1) == mga.MGA_ERR_INVALID_VALUE
+    assert _check(N=4100) == mga.MGA_ERR_LAYOUT
+    assert _check(k=A + 8) == mga.MGA_ERR_LAYOUT
+    assert _check(o=A + 2) == mga.MGA_ERR_LAYOUT
+    assert _check(splits=33) == mga.MGA_ERR_CONFIG          # ceil(4096/128) = 32
+    assert _check(B=70000, N=128) == mga.MGA_ERR_CONFIG      # grid z above 65535
+    assert _check(splits=4, ws=None) == mga.MGA_ERR_WORKSPACE
+    assert _check(splits=4, ws_bytes=1024) == mga.MGA_ERR_WORKSPACE
+    assert _check(splits=4, ws=A + 4) == mga.MGA_ERR_WORKSPACE
+    # One split needs no workspace; empty batches or rows are no-ops.
+    assert _check(splits=1, ws=None, ws_bytes=0) == mga.MGA_OK
+    assert _check(B=0, q=None, k=None, v=None, o=None, ws=None, ws_bytes=0) == mga.MGA_OK
+    assert _check(M=0, q=None, k=None, v=None, o=None, ws=None, ws_bytes=0) == mga.MGA_OK
+
+
+def test_forward_rejects_before_launching():
+    # Errors come back before any HIP call, so this runs without a GPU.
+    assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4100, 0, None, 0, None) == mga.MGA_ERR_LAYOUT
+    assert mga.mga_gqa_partial(None, A, A, A, 2, 256, 4096, 1, None, 0, None) == \
+        mga.MGA_ERR_INVALID_VALUE
+    assert mga.mga_gqa_combine(A, 2, 256, 4096, 4, None, 0, None) == mga.MGA_ERR_WORKSPACE
+    assert mga.mga_gqa_forward(None, None, None, None, 0, 256, 4096, 0, None, 0, None) == mga.MGA_OK
+
+
+@pytest.mark.parametrize("B,M,N", [(2, 256, 4096), (16, 256, 4096), (2, 256, 32768),
+                                   (64, 8, 8192), (128, 256, 16384), (1, 1, 8), (3, 17, 136),
+                                   (5, 100, 1000), (1, 300, 129 * 8)])
+def test_split_policy_and_workspace(B, M, N):
+    nblocks = math.ceil(N / mga.KEY_BLOCK)
+    s = mga.mga_gqa_choose_splits(B, M, N)
+    assert 1 <= s <= nblocks
+    for req in sorted({r for r in (0, 1, 2, 3, 7, nblocks) if r <= nblocks}):
+        eff = mga.mga_gqa_effective_splits(B, M, N, req)
+        want = s if req == 0 else req
+        chunk = math.ceil(nblocks / want)
+        assert eff == math.ceil(nblocks / chunk)
+        assert 1 <= eff <= want
+        assert (eff - 1) * chunk < nblocks          # no empty split
+        ws = mga.mga_gqa_workspace_bytes(B, M, N, req)
+        if eff == 1:
+            assert ws == 0
+        else:
+            assert ws >= eff * B * M * 65 * 4 and ws % 256 == 0 and ws - eff * B * M * 65 * 4 < 256
+    assert mga.mga_gqa_effective_splits(B, M, N, nblocks + 1) == -1
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _lib.load()
