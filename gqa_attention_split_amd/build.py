@@ -17,9 +17,10 @@ SOURCES = [os.path.join(CSRC, "gqa_kernels.hip"), os.path.join(CSRC, "mga_api.cp
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are turned off for every device compile.
+# MFMA results go to VGPRs (the scores feed VALU exp directly, no AGPR reads).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-munsafe-fp-atomics", "-Wall"]
+                "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall"]
 
 
 def build(verbose: bool = False, resource_usage: bool = False, extra=None) -> str:

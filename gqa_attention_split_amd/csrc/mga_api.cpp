@@ -21,25 +21,33 @@ namespace mga {
 namespace {
 
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kTargetGroups = 2 * kCUs;
-constexpr int kMinBlocksPerSplit = 2;
+constexpr int kTargetGroups = kCUs;  // one workgroup (4 waves, one per SIMD) per CU
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-int query_groups_for(int M) {
-    if (M > 128) return 4;
-    if (M > 64) return 2;
-    return 1;
+int variant_for(int M) {
+    if (M <= 32) return kVariantDecode;
+    if (M <= 64) return kVariantSmall;
+    if (M <= 128) return kVariantMedium;
+    return kVariantLarge;
 }
 
-// Policy: enough workgroups for two per compute unit, but at least two key
-// blocks per split so the double buffer has something to overlap.
+int rows_for(int variant) {
+    switch (variant) {
+    case kVariantDecode: return 32;
+    case kVariantSmall: return 64;
+    case kVariantMedium: return 128;
+    default: return 256;
+    }
+}
+
+// Policy: split the keys just enough that the grid reaches one workgroup per
+// compute unit; every split keeps at least one 128-key block.
 int policy_splits(int B, int M, int N) {
     if (N < 1 || B < 1 || M < 1) return 1;
     const long long nblocks = ceil_div(N, kKeyBlock);
-    const long long base = (long long)B * ceil_div(M, 64LL * query_groups_for(M));
-    long long s = ceil_div(kTargetGroups, base);
-    s = std::min(s, std::max(1LL, nblocks / kMinBlocksPerSplit));
+    const long long base = (long long)B * ceil_div(M, rows_for(variant_for(M)));
+    const long long s = std::min(ceil_div(kTargetGroups, base), nblocks);
     return (int)std::max(1LL, s);
 }
 
@@ -55,15 +63,17 @@ int make_plan(int B, int M, int N, int splits, Plan *p) {
     p->B = B;
     p->M = M;
     p->N = N;
-    p->qgroups = query_groups_for(M);
-    p->tile_rows = 64 * p->qgroups;
+    p->variant = variant_for(M);
+    p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;
     const int want = splits == 0 ? policy_splits(B, M, N) : splits;
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);
-    if (B > 65535 || p->mtiles > 65535) return MGA_ERR_CONFIG;
+    if (N > kMaxKeys) return MGA_ERR_CONFIG;
+    const long long groups = ceil_div((long long)B * p->splits, 8) * 8 * p->mtiles;
+    if (groups > INT_MAX || (long long)B * M > INT_MAX / kHeadDim) return MGA_ERR_CONFIG;
     if (p->splits > 1) {
         const size_t rows = (size_t)p->splits * B * M;
         const size_t bytes = rows * kHeadDim * sizeof(float) + rows * sizeof(float);
@@ -97,7 +107,7 @@ const char *mga_status_string(int status) {
     case MGA_ERR_LAYOUT:
         return "MGA_ERR_LAYOUT: pointer not 16-byte aligned or N not a multiple of 8";
     case MGA_ERR_CONFIG:
-        return "MGA_ERR_CONFIG: splits above ceil(N/128) or grid dimension above 65535";
+        return "MGA_ERR_CONFIG: splits above ceil(N/128), N above 2^24-1, or a grid too large";
     case MGA_ERR_WORKSPACE: return "MGA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MGA_ERR_HIP: return "MGA_ERR_HIP: kernel launch failed";
     default: return "unknown mga status";

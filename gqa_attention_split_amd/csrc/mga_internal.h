@@ -8,8 +8,8 @@ namespace mga {
 // Geometry of one launch, decided on the host before anything is enqueued.
 struct Plan {
     int B, M, N;
-    int qgroups;      // 16-row query groups per wave (1, 2 or 4); rows per workgroup = 64 * qgroups
-    int tile_rows;    // 64 * qgroups
+    int variant;      // kernel shape, one of the kVariant* values
+    int tile_rows;    // query rows per workgroup
     int mtiles;       // ceil(M / tile_rows)
     int nblocks;      // ceil(N / key block)
     int splits;       // effective split count (>= 1)
@@ -17,7 +17,16 @@ struct Plan {
     size_t ws_bytes;  // workspace the plan needs (0 when splits == 1)
 };
 
+// Kernel shapes: (query tiles of 32 per wave, query waves, key streams).
+// Every shape has 8 waves per workgroup (two per SIMD).
+constexpr int kVariantDecode = 0;  // M <= 32:  (1, 1, 8), 32 rows per workgroup
+constexpr int kVariantSmall = 1;   // M <= 64:  (2, 1, 8), 64 rows per workgroup
+constexpr int kVariantMedium = 2;  // M <= 128: (2, 2, 4), 128 rows per workgroup
+constexpr int kVariantLarge = 3;   // M > 128:  (2, 4, 2), 256 rows per workgroup
+
 constexpr int kKeyBlock = 128;
+// Buffer descriptors address one batch's K or V with 32-bit byte offsets.
+constexpr int kMaxKeys = (1 << 24) - 1;
 constexpr int kHeadDim = 64;
 constexpr int kThreads = 256;
 

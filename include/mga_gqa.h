@@ -27,13 +27,12 @@
  * The head dimension is fixed at 64. Pointers must be 16-byte aligned and N a
  * multiple of 8 (every K row then starts on a 16-byte boundary).
  *
- * Numerics: fp16 MFMA products with fp32 accumulation; exp in fp32 via the
- * hardware exp2; P = fp16(E) feeds the second product, and the row-sum is
- * taken from the same fp16 P (so numerator and denominator see identical
- * weights). Results are deterministic for a fixed (shape, splits): the
- * partials are combined in split order and no atomics are used. Inputs whose
- * scores reach ln(65504) ~ 11.09 overflow fp16 P; results are then undefined
- * (the graph itself overflows there).
+ * Numerics: fp16 MFMA products with fp32 accumulation; E = exp(A) in fp32
+ * via the hardware exp2; the row-sum adds the fp32 E; P = fp16(E), rounded to
+ * nearest even, feeds the second product. Results are deterministic for a
+ * fixed (shape, splits): every sum runs in a fixed order and no atomics are
+ * used. Inputs whose scores reach ln(65504) ~ 11.09 overflow fp16 P; results
+ * are then undefined (the graph itself overflows there).
  *
  * Ownership and asynchrony: the caller owns q, k, v, o and the workspace; the
  * library allocates and frees nothing on the device and keeps no device state,
@@ -61,7 +60,7 @@ typedef enum {
     MGA_OK = 0,
     MGA_ERR_INVALID_VALUE = 1, /* null pointer, B or M < 0, N < 1, splits < 0      */
     MGA_ERR_LAYOUT = 2,        /* pointer not 16-byte aligned, or N % 8 != 0        */
-    MGA_ERR_CONFIG = 3,        /* splits > ceil(N / 128) or a grid dimension > 65535 */
+    MGA_ERR_CONFIG = 3,        /* splits > ceil(N / 128), N > 2^24 - 1, grid too big */
     MGA_ERR_WORKSPACE = 4,     /* workspace missing, misaligned or too small        */
     MGA_ERR_HIP = 5            /* a kernel launch failed                            */
 } mga_status;

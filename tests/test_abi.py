@@ -63,7 +63,8 @@ def test_check_args_codes():
     assert _check(k=A + 8) == mga.MGA_ERR_LAYOUT
     assert _check(o=A + 2) == mga.MGA_ERR_LAYOUT
     assert _check(splits=33) == mga.MGA_ERR_CONFIG          # ceil(4096/128) = 32
-    assert _check(B=70000, N=128) == mga.MGA_ERR_CONFIG      # grid z above 65535
+    assert _check(N=1 << 24, splits=1) == mga.MGA_ERR_CONFIG   # byte offsets exceed 32 bits
+    assert _check(B=1 << 20, M=1 << 20, N=128) == mga.MGA_ERR_CONFIG
     assert _check(splits=4, ws=None) == mga.MGA_ERR_WORKSPACE
     assert _check(splits=4, ws_bytes=1024) == mga.MGA_ERR_WORKSPACE
     assert _check(splits=4, ws=A + 4) == mga.MGA_ERR_WORKSPACE
