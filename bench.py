@@ -48,8 +48,12 @@ def parse_args():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--graph-steps", type=int, default=200, help="steps captured per HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target CPU work for the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=1.5,
+                    help="target wall time of the oracle baseline sample (the whole workload "
+                         "is repeated until it is reached)")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="graph: replay captured steps (default); eager: plain launches "
+                         "(for counter collection, which sees eager dispatches)")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run one plain device-to-device copy of known size "
                          "(reference dispatch for FETCH_SIZE / WRITE_SIZE scaling)")
@@ -117,34 +121,25 @@ def time_eager(torch, stream, fn, n_steps, warmup):
 
 
 def cpu_baseline(cfg, q, k, v, target_s):
-    """The oracle as it stands, on the host's cores, on whole query rows of the
-    same workload (a row costs the same at any row index)."""
-    import numpy as np
-
+    """The oracle as it stands, on the host's cores, over the whole workload
+    (every batch row, query row and key), repeated until about `target_s`
+    seconds of wall time have passed; reports the mean rate."""
     import oracle
-    rows_per_b = cfg.M
-    # Probe one batch row's slice to size the sample.
-    probe_rows = min(cfg.M, 8)
-    t0 = time.perf_counter()
-    oracle.gqa_f64(np.ascontiguousarray(q[:1, :probe_rows]), k[:1], v[:1])
-    per_row = max((time.perf_counter() - t0) / probe_rows, 1e-9)
-    total_rows = cfg.B * rows_per_b
-    want_rows = int(min(total_rows, max(1, target_s / per_row)))
-    nb = max(1, min(cfg.B, want_rows // rows_per_b))
-    m = rows_per_b if want_rows >= rows_per_b else max(1, want_rows)
-    qs = np.ascontiguousarray(q[:nb, :m])
-    t0 = time.perf_counter()
-    oracle.gqa_f64(qs, k[:nb], v[:nb])
-    dt = time.perf_counter() - t0
-    flops = 4 * nb * m * cfg.N * cfg.D
+    reps, t_total = 0, 0.0
+    while reps == 0 or t_total < target_s:
+        t0 = time.perf_counter()
+        oracle.gqa_f64(q, k, v)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    dt = t_total / reps
     return {
-        "value": flops / dt / 1e12,
+        "value": cfg.flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": (f"{nb} of {cfg.B} batch rows x {m} of {cfg.M} query rows x all {cfg.N} keys "
-                   f"({flops / 1e9:.2f} GFLOP, {dt:.2f} s, fp64 C loops, OpenMP)"),
-        "seconds": dt,
+        "sample": (f"whole workload ({cfg.B}x{cfg.M} query rows x {cfg.N} keys, "
+                   f"{cfg.flops / 1e9:.2f} GFLOP) x {reps} repeats, {dt:.3f} s each; "
+                   "fp64 C loops, OpenMP over query rows"),
     }
 
 
@@ -202,15 +197,32 @@ def main():
           f"({R * set_bytes / 2**20:.0f} MiB) steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
     gsteps = max(1, min(args.graph_steps, args.steps))
+
+    def combine(i, rotate=True):
+        j = i % R if rotate else 0
+        rc = lib.mga_gqa_combine(optr[j], B, M, N, splits, ws_ptr, ws_bytes, sh)
+        if rc:
+            raise mga.GqaError(rc)
+
+    def timed(fn):
+        if args.mode == "graph":
+            return time_graph(torch, stream, fn, args.steps, gsteps, args.warmup)[0]
+        return time_eager(torch, stream, fn, args.steps, args.warmup)
+
     with torch.cuda.stream(stream):
-        ms_step, timed = time_graph(torch, stream, fwd, args.steps, gsteps, args.warmup)
+        ms_step = timed(fwd)
+        timed_steps = args.steps if args.mode == "eager" else \
+            max(1, math.ceil(args.steps / gsteps)) * gsteps
         print(f"[bench] forward {ms_step * 1e3:.3f} us/step", file=sys.stderr, flush=True)
-        ms_partial, _ = time_graph(torch, stream, partial, args.steps, gsteps, args.warmup)
+        ms_partial = timed(partial)
         print(f"[bench] partial kernel {ms_partial * 1e3:.3f} us/launch", file=sys.stderr, flush=True)
-        ms_hot, _ = time_graph(torch, stream, lambda i: fwd(i, rotate=False), args.steps, gsteps,
-                               args.warmup)
-        ms_eager = time_eager(torch, stream, fwd, args.steps, args.warmup) if args.eager else None
+        ms_combine = timed(combine) if eff > 1 else 0.0
+        ms_hot = timed(lambda i: fwd(i, rotate=False))
+        ms_eager = time_eager(torch, stream, fwd, args.steps, args.warmup) \
+            if args.eager and args.mode == "graph" else None
         if args.pmc_calibrate:
+            # One plain device-to-device copy of known size: the reference
+            # dispatch that FETCH_SIZE / WRITE_SIZE readings are scaled by.
             src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
             dst.copy_(src)
@@ -235,7 +247,7 @@ def main():
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": timed,
+        "steps": timed_steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
@@ -245,12 +257,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "M": M, "N": N, "D": cfg.D,
                    "q_k_std": cfg.qk_std, "v_dist": cfg.v_dist, "seed": cfg.seed,
-                   "splits": eff, "rotating_sets": R, "timing": "hip-graph replay, events on the launch stream"},
+                   "splits": eff, "rotating_sets": R,
+                   "timing": ("hip-graph replay" if args.mode == "graph" else "eager launches")
+                   + ", events on the launch stream"},
         "hbm_gbps": round(gbps, 1),
         "frac_hbm_peak": round(t_hbm / s, 4),
         "frac_mfma_peak": round(t_mfma / s, 4),
         "hot_ms_per_step": round(ms_hot, 6),
         "partial_kernel_ms": round(ms_partial, 6),
+        "combine_kernel_ms": round(ms_combine, 6),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": read_traffic(cfg.name),
                      "kernel": "gqa_partial_kernel"},
@@ -259,7 +274,6 @@ def main():
         result["eager_ms_per_step"] = round(ms_eager, 6)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
-        cb.pop("seconds")
         cb["value"] = round(cb["value"], 6)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
