@@ -65,6 +65,14 @@ def mga_gqa_workspace_bytes(B: int, M: int, N: int, splits: int) -> int:
     return _lib.load().mga_gqa_workspace_bytes(B, M, N, splits)
 
 
+def mga_gqa_plan(B: int, M: int, N: int, splits: int):
+    """(status, tile_rows, effective_splits) for a shape."""
+    import ctypes
+    rows, eff = ctypes.c_int(0), ctypes.c_int(0)
+    rc = _lib.load().mga_gqa_plan(B, M, N, splits, ctypes.byref(rows), ctypes.byref(eff))
+    return rc, rows.value, eff.value
+
+
 def mga_gqa_check_args(q, k, v, o, B, M, N, splits, ws, ws_bytes) -> int:
     return _lib.load().mga_gqa_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
                                           _ptr(ws), ws_bytes)
@@ -128,9 +136,8 @@ def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None)
     elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, HEAD_DIM) or \
             not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous float16 (B, M, 64) tensor on q's device")
-    need = mga_gqa_workspace_bytes(B, M, N, splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(B, M, N, splits, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)

@@ -6,41 +6,52 @@
 // Split-KV form (kaispace blog, sections 2.1 and 4.2-4.3: a for-loop over the
 // key dimension that accumulates, then a combine block graph): a workgroup
 // owns (batch row b, query tile, key chunk) and accumulates
-//   W = sum_n fp16(e_n) V[n]   and   L = sum_n e_n
+//   W = sum_n P_n V[n]   and   L = sum_n P_n,   P_n = fp16(exp(a_n))
 // over its chunk; O = sum_s W_s / sum_s L_s. With no running maximum the
 // partials combine by plain sums.
 //
 // Partial kernel. A workgroup has QW x KS waves: QW query groups of 32*QT
-// rows each, times KS key streams. Stream ks takes every KS-th 32-key tile of
-// the chunk; its QW waves share that tile through LDS. Per tile and wave:
+// rows each, times KS key streams; stream ks takes every KS-th 32-key tile
+// of the chunk. Per tile and wave:
 //   * S^T = K^T Q^T on v_mfma_f32_32x32x16_f16: keys on the accumulator rows,
 //     queries on its columns; Q^T stays in registers for the whole kernel.
 //   * E = exp2(S') in fp32, where S' = (log2(e) Q) K comes from Q pre-scaled
-//     once per workgroup; L += E (fp32 adds); P = fp16(E) (nearest even). In the 32x32 accumulator layout a lane holds 16 keys of one
-//     query, in exactly the order the next MFMA's B operand needs (two 16-key
-//     k-steps, 8 consecutive accumulator registers each), so the scores never
-//     leave registers.
+//     once per workgroup; P = fp16(E) rounded to nearest even; L += P in fp32
+//     (v_dot2_f32_f16 against (1, 1)). In the 32x32 accumulator layout a lane
+//     holds 16 keys of one query in exactly the order the next MFMA's B
+//     operand needs (two 16-key k-steps, 8 consecutive accumulator registers
+//     each), so the scores never leave registers.
 //   * O^T += V^T P^T on the same MFMA.
-// K (head-dim-major) and V (key-major) are copied HBM -> LDS as they are laid
-// out in memory, by buffer_load ... lds (no registers involved), into a ring
-// of 4 buffers (two tiles per stream in flight ahead of the pair being
-// computed). The MFMA operands need the contraction index along each lane's
-// 8 values, which is the slow index of both tiles; ds_read_b64_tr_b16
-// delivers that transpose: within each group of 16 lanes it returns
+// K (head-dim-major), V (key-major) and Q are copied HBM -> LDS as they lie in
+// memory by buffer_load ... lds, which moves no data through registers. The
+// MFMA operands need the contraction index along each lane's 8 values, the
+// slow index of both K and V tiles; ds_read_b64_tr_b16 delivers that
+// transpose: within each group of 16 lanes it returns
 // result[i][j] = source[4j + i/4][i % 4] over the 16 lanes' 4-element reads,
 // i.e. lane i receives column i of a 4 x 16 block. LDS rows are XOR-swizzled
 // at 32-byte granularity so that the four rows of such a block fall in
 // distinct banks.
+//
+// Two ring disciplines:
+//   * private (QW == 1): each wave owns its key stream and a two-tile LDS
+//     ring; the loop has no workgroup barrier. A tile's operands are read into
+//     registers first, which frees its buffer for the tile two ahead before
+//     any of its MFMAs run.
+//   * shared (QW > 1): the QW waves of a stream share each tile; a ring of
+//     STAGES tiles per stream, one workgroup barrier per step, and a
+//     three-phase software pipeline (first product of tile it, softmax of
+//     it-1, second product of it-2).
 // After the loop the KS streams of a query group are summed in LDS in a fixed
 // order; with one split the kernel writes O = fp16(W / L), otherwise W and L
 // go to the caller's workspace for the combine kernel.
 //
-// Bounds. Every K/V access goes through a buffer descriptor that covers only
-// batch b's K (or V) array: keys past N read as zero (V) or as other keys of
-// the same batch (K, whose rows continue in memory); either way the scores of
-// keys past the chunk end are forced to E = 0. Tiles wholly past the chunk
-// end are issued with an offset past the descriptor's end, so they move no
-// data and write zeros. Query rows past M are zero-filled and never stored.
+// Bounds. K/V/Q accesses go through buffer descriptors whose record count
+// ends at the last valid byte of batch b's array (or at zero for tiles past
+// the chunk end), so out-of-range lanes read zeros. K rows continue into the
+// next row in memory, so in a tile that straddles N the lanes whose keys lie
+// past N get an offset beyond the descriptor. Keys read as zero K columns and
+// zero V rows have S = 0 and P = 1 and contribute nothing to W; they are
+// counted and removed from L. Query rows past M are zero and never stored.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,9 +78,15 @@ constexpr int TILE_BYTES = KT * HD * 2 * 2;  // K part 4 KiB + V part 4 KiB
 constexpr int K_ROW_BYTES = KT * 2;          // 64
 constexpr int V_ROW_BYTES = HD * 2;          // 128
 constexpr int V_PART = KT * HD * 2;          // byte offset of the V part in a tile
+constexpr int Q_ROW_BYTES = HD * 2;          // 128
 constexpr int RED_ROW_BYTES = HD * 4 + 16;   // fp32 row of 64 + 16-byte pad (bank spread)
+constexpr int LDS_LIMIT = 160 * 1024;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int BUFFER_FLAGS = 0x00020000;     // gfx9 raw buffer descriptor, dword 3
+constexpr uint32_t OOB = 0x80000000u;        // offset past every descriptor's records
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 __device__ __forceinline__ half8 cat8(fp16x4 lo, fp16x4 hi) {
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
@@ -92,31 +109,34 @@ __device__ __forceinline__ int v_off(int key, int col_byte) {
 }
 
 template <int QT, int QW, int KS>
-struct Partial {
+struct Cfg {
     static constexpr int NWAVES = QW * KS;
-    static constexpr int ROWS = 32 * QT * QW;  // query rows per workgroup
+    static constexpr int ROWS = 32 * QT * QW;   // query rows per workgroup
     static_assert(4 % QW == 0, "QW must divide the 4 K and 4 V DMA instructions of a tile");
-    static constexpr int PER = 4 / QW;         // K (and V) DMA instructions per wave per tile
-    // LDS ring: each buffer holds one tile per stream. Step `it` reads tile it
-    // only, so after its barrier the buffer of tile it-1 is free and is
-    // refilled with tile it+STAGES-1: STAGES-1 tiles are in flight.
+    static_assert(KS >= 2, "streams");
+    static constexpr int PER = 4 / QW;          // K (and V) DMA instructions per wave per tile
+    static constexpr int TILE_OPS = 2 * PER;    // DMA instructions per wave per tile
+    static constexpr bool PRIVATE = QW == 1;
+    // Shared ring: each buffer holds one tile per stream; step `it` refills
+    // the buffer of tile it-3, so DIST = STAGES - 3 tiles are in flight.
     static constexpr int STAGE_BYTES = KS * TILE_BYTES;
+    static constexpr int STAGES = PRIVATE ? 2 : cmin(LDS_LIMIT / STAGE_BYTES, 10);
+    static constexpr int DIST = PRIVATE ? 2 : STAGES - 3;
+    static constexpr int RING_BYTES = PRIVATE ? NWAVES * 2 * TILE_BYTES : STAGES * STAGE_BYTES;
+    // Q staging: past the private rings, or in shared-ring buffers that the
+    // prologue leaves empty (DIST .. STAGES-1).
+    static constexpr int Q_BYTES = ROWS * Q_ROW_BYTES;
+    static constexpr int Q_OFF = PRIVATE ? RING_BYTES : DIST * STAGE_BYTES;
+    static constexpr int Q_OPS = ROWS / 8;      // 1 KiB DMA instructions for the workgroup's Q
     static constexpr int RED_BYTES = 32 * QT * RED_ROW_BYTES + 32 * QT * 4;  // one wave's epilogue region
-    static constexpr int STAGES = (160 * 1024) / STAGE_BYTES < 10 ? (160 * 1024) / STAGE_BYTES : 10;
-    // With 4 or fewer streams the ring is deep enough for the three-phase
-    // software pipeline (a step reads tiles it and it-2 and keeps it-1, so it
-    // refills tile it-3's buffer); with 8 streams each step handles one tile
-    // and refills the buffer of tile it-1.
-    static constexpr bool PIPE = STAGES >= 5;
-    static constexpr int DIST = PIPE ? STAGES - 3 : STAGES - 1;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES > NWAVES * RED_BYTES ? STAGES * STAGE_BYTES
-                                                                              : NWAVES * RED_BYTES;
-    static_assert(STAGES >= 2, "ring depth");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert((DIST - 1) * 2 * PER < 64, "vmcnt range");
+    static constexpr int LDS_BYTES = cmax(cmax(RING_BYTES, Q_OFF + Q_BYTES), NWAVES * RED_BYTES);
     static constexpr int DW = HD / KS;                // head dims each wave finalises
     static constexpr int VPL = 32 * QT * DW / 64;     // values per lane in the final write
-    static_assert(KS == 1 || (VPL >= 4 && VPL % 4 == 0), "final write granularity");
+    static_assert(PRIVATE || STAGES >= 5, "shared ring depth");
+    static_assert(PRIVATE || Q_OFF + Q_BYTES <= RING_BYTES, "Q staging inside the free ring buffers");
+    static_assert(LDS_BYTES <= LDS_LIMIT, "LDS budget");
+    static_assert(DIST * TILE_OPS < 64, "vmcnt range");
+    static_assert(VPL >= 4 && VPL % 4 == 0, "final write granularity");
 };
 
 // gfx9 raw buffer descriptor: 48-bit base, stride 0, `bytes` records, so
@@ -134,7 +154,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *p, uint32_t bytes) {
 // One buffer_load_dwordx4 ... lds: lane l's 16 bytes land at LDS byte
 // address lds + 16 l. Issued through asm so that the compiler neither waits
 // for these loads before unrelated LDS reads nor reorders memory accesses
-// across them; completion is waited for explicitly (sync_tile).
+// across them; completion is waited for explicitly (wait_vm / sync_tile).
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
@@ -143,42 +163,87 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
 }
 
 // Wait until at most N of this wave's vector-memory operations are
-// outstanding, then meet the other waves at the workgroup barrier.
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// ... then meet the other waves at the workgroup barrier.
 template <int N>
 __device__ __forceinline__ void sync_tile() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
+// Every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-// Issue this wave's DMA share of one stream's tile (keys ts .. ts+31) into
-// the LDS tile at byte address `lds`. A tile is 8 instructions of 64 lanes x
-// 16 bytes: 4 fill the K part (16 rows of 64 bytes each), 4 the V part (8 rows
-// of 128 bytes each); each of the QW waves sharing the tile issues 4/QW of
-// each. Key chunks at or past N, and whole tiles at or past the chunk end,
-// are given an offset past the descriptor and read zero.
+// Per-lane DMA offsets of this wave's share of a tile (independent of the
+// tile's position: the descriptor base moves instead). K instruction x fills
+// K rows 16 r .. 16 r + 15 (r = qw*PER + x), 4 lanes per 64-byte row; V
+// instruction x fills V rows 8 r .. 8 r + 7, 8 lanes per 128-byte row. A lane
+// fetches the 16-byte unit that the row's swizzle puts at its position.
 template <int QW>
-__device__ __forceinline__ void issue_tile(i32x4 krsrc, i32x4 vrsrc, uint32_t lds, int N, int ts,
-                                           int kend, int qw, int lane) {
+struct TileDma {
+    static constexpr int PER = 4 / QW;
+    uint32_t koff[PER];  // byte offset of the lane's 8 keys of head dim d from the tile's key 0
+    uint32_t kcol;       // first key of those 8, relative to the tile start
+    uint32_t voff;       // byte offset within the tile's 32 x 64 V block (instruction 0)
+};
+template <int QW>
+__device__ __forceinline__ TileDma<QW> make_tile_dma(int qw, int lane, int N) {
     constexpr int PER = 4 / QW;
-    const bool live = ts < kend;
-    const uint32_t oob = (uint32_t)N * (HD * 2);
+    TileDma<QW> t;
+    const uint32_t lc = (lane & 3) ^ (((lane >> 3) & 1) << 1);  // bit 1 of d = bit 3 of lane
+    t.kcol = 8 * lc;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-        const int r = qw * PER + x;  // K rows 16r .. 16r+15
-        const uint32_t d = 16 * r + (lane >> 2);
-        const uint32_t lc = (lane & 3) ^ (((d >> 1) & 1) << 1);
-        const uint32_t key = (uint32_t)ts + 8 * lc;
-        const uint32_t off = live && key < (uint32_t)N ? (d * (uint32_t)N + key) * 2 : oob;
-        dma16(krsrc, off, lds + r * 1024);
+        const uint32_t d = 16 * (qw * PER + x) + (lane >> 2);
+        t.koff[x] = (d * (uint32_t)N + t.kcol) * 2;
     }
+    const uint32_t kr = 8 * (qw * PER) + (lane >> 3);
+    const uint32_t vc = (lane & 7) ^ ((kr & 3) << 1);
+    t.voff = (kr * HD + 8 * vc) * 2;
+    return t;
+}
+
+// Issue this wave's DMA share of one stream's tile (keys key0 .. key0+31 of
+// the batch whose K and V arrays start at kb and vb) into the LDS tile at
+// byte address `lds`. `live` is false for tiles past the chunk end: their
+// descriptors hold zero records and the tile fills with zeros without
+// touching memory. The descriptors start at the tile and end with the batch.
+template <int QW>
+__device__ __forceinline__ void issue_tile(const _Float16 *kb, const _Float16 *vb, int N, int key0,
+                                           bool live, uint32_t lds, int qw, const TileDma<QW> &t) {
+    constexpr int PER = 4 / QW;
+    const int rem = N - key0;  // keys from key0 to the end of the batch (> 0 when live)
+    const i32x4 kr = make_rsrc(kb + key0, live ? (uint32_t)(HD * N - key0) * 2 : 0u);
+    const i32x4 vr = make_rsrc(vb + (size_t)key0 * HD, live ? (uint32_t)rem * (HD * 2) : 0u);
+    const bool kin = (int)t.kcol < rem;
 #pragma unroll
-    for (int x = 0; x < PER; ++x) {
-        const int r = qw * PER + x;  // V rows 8r .. 8r+7
-        const uint32_t kr = 8 * r + (lane >> 3);
-        const uint32_t lc = (lane & 7) ^ ((kr & 3) << 1);
-        const uint32_t off = live ? (((uint32_t)ts + kr) * HD + 8 * lc) * 2 : oob;
-        dma16(vrsrc, off, lds + V_PART + r * 1024);
-    }
+    for (int x = 0; x < PER; ++x) dma16(kr, kin ? t.koff[x] : OOB, lds + (qw * PER + x) * 1024);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) dma16(vr, t.voff + x * 1024, lds + V_PART + (qw * PER + x) * 1024);
+}
+
+// Keys of a chunk of `len` keys that fall into this stream's first `nt` tiles
+// (tile it of stream ks starts at key (it*KS + ks)*32 of the chunk).
+template <int KS>
+__device__ __forceinline__ int live_keys(int len, int ks, int nt) {
+    const int full_tiles = len / KT, rem = len % KT;
+    int live = full_tiles > ks ? KT * cmin(nt, (full_tiles - ks + KS - 1) / KS) : 0;
+    if (rem != 0 && full_tiles >= ks && (full_tiles - ks) % KS == 0 && (full_tiles - ks) / KS < nt) live += rem;
+    return live;
+}
+
+// Returns the LDS byte offset x (< 2^18) unchanged, but the compiler must
+// assume it changed: used on a per-lane LDS base inside the loop so that it
+// is not hoisted as base + each read's constant (one register and one add per
+// read per step). The mask shows the value is non-negative, which lets each
+// read's constant go into the instruction's offset field.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x & 0x3ffff;
 }
 
 // Per-lane LDS byte offsets (within a tile) of the transposed operand reads.
@@ -199,14 +264,26 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
     return r;
 }
 
-// First product of one tile for one wave (32*QT queries): S^T = K^T Q^T.
-template <int QT>
-__device__ __forceinline__ void tile_scores(const char *kb, const half8 (&qf)[QT][4],
-                                            float16v (&s)[QT]) {
-    half8 a[4];
+// A operands of the first product (K^T, four 16-deep k-steps) and of the
+// second product (V^T: [t][dt] = keys 16t.., head dims 32dt..).
+__device__ __forceinline__ void read_k(const char *kb, half8 (&a)[4]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
         a[kk] = cat8(tr_read(kb + kk * 16 * K_ROW_BYTES), tr_read(kb + kk * 16 * K_ROW_BYTES + 4 * K_ROW_BYTES));
+}
+__device__ __forceinline__ void read_v(const char *vb0, const char *vb1, half8 (&a)[2][2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const char *vb = (dt == 0 ? vb0 : vb1) + t * 16 * V_ROW_BYTES;
+            a[t][dt] = cat8(tr_read(vb), tr_read(vb + 8 * V_ROW_BYTES));
+        }
+}
+
+// First product of one tile for one wave (32*QT queries): S^T = K^T Q^T.
+template <int QT>
+__device__ __forceinline__ void scores(const half8 (&a)[4], const half8 (&qf)[QT][4], float16v (&s)[QT]) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         s[qt] = float16v{};
@@ -217,32 +294,25 @@ __device__ __forceinline__ void tile_scores(const char *kb, const half8 (&qf)[QT
 }
 
 // Softmax numerators of one tile: E = exp2(S) (scores are in log2 units),
-// L += E, P = fp16(E) rounded to nearest. In the 32x32 accumulator layout
+// P = fp16(E) rounded to nearest, L += P. In the 32x32 accumulator layout
 // register r of lane l holds key 8*(r/4) + 4*(l/32) + r%4 of query l%32, so
 // registers 8t..8t+7 are exactly the 8 k-slots of the second product's
 // B operand for keys 16t..16t+15.
 template <int QT>
-__device__ __forceinline__ void tile_softmax(const float16v (&s)[QT], half8 (&p)[QT][2],
-                                             float (&lsum)[QT]) {
+__device__ __forceinline__ void softmax(const float16v (&s)[QT], half8 (&p)[QT][2], float (&lsum)[QT][2]) {
+    const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[qt][r]);
-        float a0 = 0.f, a1 = 0.f;  // two short chains instead of one long one
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            a0 += e[r];
-            a1 += e[r + 1];
-        }
-        lsum[qt] += a0 + a1;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const half2v hv = __builtin_convertvector(float2v{e[8 * t + 2 * j], e[8 * t + 2 * j + 1]}, half2v);
+                const float e0 = __builtin_amdgcn_exp2f(s[qt][8 * t + 2 * j]);
+                const float e1 = __builtin_amdgcn_exp2f(s[qt][8 * t + 2 * j + 1]);
+                const half2v hv = __builtin_convertvector(float2v{e0, e1}, half2v);
                 p[qt][t][2 * j] = hv[0];
                 p[qt][t][2 * j + 1] = hv[1];
+                lsum[qt][t] = __builtin_amdgcn_fdot2(hv, ones, lsum[qt][t], false);
             }
         }
     }
@@ -250,19 +320,14 @@ __device__ __forceinline__ void tile_softmax(const float16v (&s)[QT], half8 (&p)
 
 // Second product of one tile: O^T += V^T P^T.
 template <int QT>
-__device__ __forceinline__ void tile_pv(const char *vb0, const char *vb1, const half8 (&p)[QT][2],
-                                        float16v (&oacc)[2][QT]) {
+__device__ __forceinline__ void pv(const half8 (&a)[2][2], const half8 (&p)[QT][2], float16v (&oacc)[2][QT]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            const char *vb = (dt == 0 ? vb0 : vb1) + t * 16 * V_ROW_BYTES;
-            const half8 a = cat8(tr_read(vb), tr_read(vb + 8 * V_ROW_BYTES));
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
-                oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p[qt][t], oacc[dt][qt], 0, 0, 0);
-        }
-    }
+                oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t][dt], p[qt][t], oacc[dt][qt], 0, 0, 0);
 }
 
 template <int QT, int QW, int KS>
@@ -270,8 +335,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const _Float16 *__restrict__ q, const _Float16 *__restrict__ k,
     const _Float16 *__restrict__ v, _Float16 *__restrict__ o, float *__restrict__ ws_w,
     float *__restrict__ ws_l, int B, int M, int N, int chunk_keys, int nsplit, int mtiles) {
-    using C = Partial<QT, QW, KS>;
-    constexpr int STAGES = C::STAGES, DIST = C::DIST, SB = C::STAGE_BYTES;
+    using C = Cfg<QT, QW, KS>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     // Workgroup -> (batch, split, query tile). Consecutive workgroup ids go to
@@ -280,7 +344,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const int wid = blockIdx.x;
     const int pair = (wid / (8 * mtiles)) * 8 + (wid & 7);
     const int mtile = (wid >> 3) % mtiles;
-    if (pair >= B * nsplit) return;
+    if (pair >= B * nsplit) return;  // whole workgroup: padding of the last group of 8
     const int b = pair / nsplit, split = pair - b * nsplit;
 
     const int tid = threadIdx.x;
@@ -289,67 +353,111 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const int h = lane >> 5;
 
     const int kstart = split * chunk_keys;
-    const int kend = min(N, kstart + chunk_keys);
-    const int niter = (kend - kstart + KS * KT - 1) / (KS * KT);
+    const int len = min(N, kstart + chunk_keys) - kstart;  // keys in this chunk (> 0)
+    const int qrow0 = mtile * C::ROWS;                     // first query row of the workgroup
+    const int qbase = qrow0 + qw * 32 * QT;                // first query row of this wave
 
-    const int qbase = mtile * C::ROWS + qw * 32 * QT;  // first query row of this wave
-
-    const i32x4 krsrc = make_rsrc(k + (size_t)b * HD * N, (uint32_t)N * HD * 2);
-    const i32x4 vrsrc = make_rsrc(v + (size_t)b * N * HD, (uint32_t)N * HD * 2);
+    const _Float16 *kb = k + (size_t)b * HD * N;  // batch b's K [64][N] and V [N][64]
+    const _Float16 *vb = v + (size_t)b * N * HD;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)(smem));
     const LaneOffsets lo = lane_offsets(lane);
+    const TileDma<QW> td = make_tile_dma<QW>(qw, lane, N);
 
-    // Pre-loop: Q^T fragments (B operand). Lane holds query qbase + 32*qt +
-    // (lane & 31), head dims 16*kk + 8*h .. +7, pre-scaled by log2(e) (fp32
-    // product rounded to fp16) so that the first product yields log2-domain
-    // scores and E = exp2(S) needs no per-score multiply.
-    half8 qf[QT][4];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        const int row = qbase + 32 * qt + (lane & 31);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            half8 x = row < M ? *reinterpret_cast<const half8 *>(q + ((size_t)b * M + row) * HD + 16 * kk + 8 * h)
-                              : half8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = (_Float16)((float)x[j] * LOG2E);
-            qf[qt][kk] = x;
-        }
+    // Tiles are numbered per stream: tile it of stream ks starts at chunk key
+    // (it*KS + ks)*32. `ntiles` counts the tiles a stream visits.
+    const int chunk_tiles = (len + KT - 1) / KT;
+    const int ntiles = C::PRIVATE ? (chunk_tiles > ks ? (chunk_tiles - ks + KS - 1) / KS : 0)
+                                  : (len + KS * KT - 1) / (KS * KT);
+    auto tile_key = [&](int it) { return (it * KS + ks) * KT; };  // relative to kstart
+    auto issue = [&](int it, uint32_t lds) {
+        issue_tile<QW>(kb, vb, N, kstart + tile_key(it), it < ntiles && tile_key(it) < len, lds, qw, td);
+    };
+
+    // Q for the workgroup's rows -> LDS (rows past M read zero). Issued before
+    // any K/V tile so that the first step finds it.
+    {
+        const int qrows = min(C::ROWS, M - qrow0);
+        const i32x4 qr = make_rsrc(q + ((size_t)b * M + qrow0) * HD, (uint32_t)qrows * Q_ROW_BYTES);
+        for (int j = wave; j < C::Q_OPS; j += C::NWAVES)
+            dma16(qr, (uint32_t)(j * 1024 + lane * 16), lds0 + C::Q_OFF + j * 1024);
     }
 
     float16v oacc[2][QT];
-    float lsum[QT];  // per lane: its 16 keys of every tile
+    float lsum[QT][2];  // per lane: its 16 keys of every tile, two chains
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         oacc[0][qt] = float16v{};
         oacc[1][qt] = float16v{};
-        lsum[qt] = 0.f;
+        lsum[qt][0] = 0.f;
+        lsum[qt][1] = 0.f;
     }
-
-    auto tile_start = [&](int it) { return kstart + (it * KS + ks) * KT; };
-    // Tiles are issued in order; buffer (it % STAGES) holds tile it.
-    int fill_buf = 0;   // buffer receiving the next issued tile
-    int fill_it = 0;    // next tile to issue
-    auto issue_next = [&]() {
-        issue_tile<QW>(krsrc, vrsrc, lds0 + fill_buf * SB + ks * TILE_BYTES, N, tile_start(fill_it), kend,
-                       qw, lane);
-        fill_buf = fill_buf + 1 == STAGES ? 0 : fill_buf + 1;
-        ++fill_it;
+    half8 qf[QT][4];
+    // Q^T fragments (B operand): lane holds query qbase + 32*qt + (lane & 31),
+    // head dims 16*kk + 8*h .. +7, pre-scaled by log2(e) (fp32 product rounded
+    // to fp16) so that the first product yields log2-domain scores and
+    // E = exp2(S) needs no per-score multiply.
+    auto load_q = [&]() {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const char *row = smem + C::Q_OFF + (qbase - qrow0 + 32 * qt + (lane & 31)) * Q_ROW_BYTES + 16 * h;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                half8 x = *reinterpret_cast<const half8 *>(row + 32 * kk);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (_Float16)((float)x[j] * LOG2E);
+                qf[qt][kk] = x;
+            }
+        }
+        wait_lds();
     };
-    for (int j = 0; j < DIST; ++j) issue_next();
 
-    // Keys at or past the chunk end were loaded as zero K columns and zero V
-    // rows: their S is 0, their E exactly 1 and their O contribution nothing;
-    // they are removed from L by count at the end.
-    float masked = 0.f;
-    auto count_masked = [&](int it) { masked += (float)min(KT, max(0, tile_start(it) + KT - kend)); };
-    auto tile_at = [&](int it) { return smem + (it % STAGES) * SB + ks * TILE_BYTES; };
-    auto sync = [&]() {
-        sync_tile<(DIST - 1) * 2 * C::PER>();  // tile it landed for every wave; its refill target is free
-        issue_next();
-    };
-    if constexpr (C::PIPE) {
+    if constexpr (C::PRIVATE) {
+        // Wave-private ring: buffers ring0 and ring0 + TILE_BYTES.
+        const uint32_t ring0 = lds0 + wave * 2 * TILE_BYTES;
+        const char *ring = smem + wave * 2 * TILE_BYTES;
+        issue(0, ring0);
+        issue(1, ring0 + TILE_BYTES);
+        sync_tile<2 * C::TILE_OPS>();  // this wave's Q share landed; barrier: all of Q landed
+        load_q();
+        for (int it = 0; it < ntiles; ++it) {
+            wait_vm<C::TILE_OPS>();  // tile it landed (tile it+1 may still be in flight)
+            const char *buf = ring + (it & 1) * TILE_BYTES;
+            half8 ka[4], va[2][2];
+            read_k(buf + lo.k, ka);
+            read_v(buf + lo.v[0], buf + lo.v[1], va);
+            wait_lds();              // the buffer is free: refill it with tile it+2
+            issue(it + 2, ring0 + (it & 1) * TILE_BYTES);
+            float16v s[QT];
+            half8 p[QT][2];
+            scores<QT>(ka, qf, s);
+            softmax<QT>(s, p, lsum);
+            pv<QT>(va, p, oacc);
+        }
+        wait_vm<0>();
+        __syncthreads();  // every ring and the Q staging are free for the reduction
+    } else {
+        constexpr int STAGES = C::STAGES, DIST = C::DIST, SB = C::STAGE_BYTES;
+        int fill_buf = 0;  // buffer receiving the next issued tile
+        int fill_it = 0;   // next tile to issue
+        auto issue_next = [&]() {
+            issue(fill_it, lds0 + fill_buf * SB + ks * TILE_BYTES);
+            fill_buf = fill_buf + 1 == STAGES ? 0 : fill_buf + 1;
+            ++fill_it;
+        };
+        for (int j = 0; j < DIST; ++j) issue_next();
+        sync_tile<DIST * C::TILE_OPS>();  // this wave's Q share landed; barrier: all of Q landed
+        load_q();                        // done before the first refill overwrites the staging
+
+        // Unsigned index arithmetic lets the compiler fold each read's constant
+        // part into the LDS instruction's offset field.
+        auto tile_at = [&](int it) {
+            return smem + ((unsigned)it % (unsigned)STAGES) * (unsigned)SB + (unsigned)ks * (unsigned)TILE_BYTES;
+        };
+        auto sync = [&]() {
+            sync_tile<(DIST - 1) * C::TILE_OPS>();  // tile it landed for every wave; its refill target is free
+            issue_next();
+        };
         // Step `it` runs the first product of tile it, the softmax numerators
         // of tile it-1 and the second product of tile it-2. The three are
         // independent, so each wave's instruction stream always holds both
@@ -358,34 +466,39 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         // the scores alternate between s0 and s1.
         float16v s0[QT], s1[QT];
         half8 p[QT][2];
-        auto g1 = [&](int it, float16v (&sv)[QT]) { tile_scores<QT>(tile_at(it) + lo.k, qf, sv); };
-        auto sm = [&](int it, const float16v (&sv)[QT]) {
-            tile_softmax<QT>(sv, p, lsum);
-            count_masked(it);
+        auto g1 = [&](int it, float16v (&sv)[QT]) {
+            half8 a[4];
+            read_k(tile_at(it) + opaque(lo.k), a);
+            scores<QT>(a, qf, sv);
         };
-        auto g2 = [&](int it) { tile_pv<QT>(tile_at(it) + lo.v[0], tile_at(it) + lo.v[1], p, oacc); };
-
+        auto sm = [&](const float16v (&sv)[QT]) { softmax<QT>(sv, p, lsum); };
+        auto g2 = [&](int it) {
+            half8 a[2][2];
+            read_v(tile_at(it) + opaque(lo.v[0]), tile_at(it) + opaque(lo.v[1]), a);
+            pv<QT>(a, p, oacc);
+        };
+        const int niter = ntiles;
         sync();                 // step 0
         g1(0, s0);
         sync();                 // step 1 (tile 1 may lie past the chunk: zeros, unused)
         g1(1, s1);
-        sm(0, s0);
+        sm(s0);
         int it = 2;
         for (; it + 1 < niter; it += 2) {
             sync();
             g2(it - 2);
             g1(it, s0);
-            sm(it - 1, s1);
+            sm(s1);
             sync();
             g2(it - 1);
             g1(it + 1, s1);
-            sm(it, s0);
+            sm(s0);
         }
         if (it < niter) {       // one more full step, it even
             sync();
             g2(it - 2);
             g1(it, s0);
-            sm(it - 1, s1);
+            sm(s1);
             ++it;
         }
         // Drain: tiles niter-2 and niter-1 still need their second product,
@@ -394,85 +507,44 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             g2(0);
         } else if (it & 1) {    // last step even: tile niter-1's scores in s0
             g2(niter - 2);
-            sm(niter - 1, s0);
+            sm(s0);
             g2(niter - 1);
         } else {                // last step odd: tile niter-1's scores in s1
             g2(niter - 2);
-            sm(niter - 1, s1);
+            sm(s1);
             g2(niter - 1);
         }
-    } else {
-        int cur = 0;  // buffer of tile it
-        for (int it = 0; it < niter; ++it) {
-            sync();   // tile it landed for every wave; tile it-1's buffer is free
-            const char *tile = smem + cur * SB + ks * TILE_BYTES;
-            float16v s[QT];
-            half8 p[QT][2];
-            tile_scores<QT>(tile + lo.k, qf, s);
-            tile_softmax<QT>(s, p, lsum);
-            tile_pv<QT>(tile + lo.v[0], tile + lo.v[1], p, oacc);
-            count_masked(it);
-            cur = cur + 1 == STAGES ? 0 : cur + 1;
-        }
+        sync_tile<0>();  // no DMA in flight, every wave done with the ring
     }
-    sync_tile<0>();  // no DMA in flight, every wave done with the ring
 
-    if constexpr (KS == 1) {
-        // One key stream: each wave owns its queries' sums outright. Lane
-        // holds O^T[d = 32*dt + 8*rb + 4*h + 0..3][query 32*qt + (lane & 31)].
+    // Keys of this stream's tiles that lie outside the chunk or past N read
+    // as zeros and entered L as P = 1 each.
+    const float masked = (float)(KT * ntiles - live_keys<KS>(len, ks, ntiles));
+
+    // Sum the KS streams of each query group in LDS (fixed order), then
+    // write O (one split) or the partial W, L.
+    {
+        char *reg = smem + wave * C::RED_BYTES;
+        float *lreg = (float *)(reg + 32 * QT * RED_ROW_BYTES);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-            const int row = qbase + 32 * qt + (lane & 31);
-            const float l = lsum[qt] + __shfl_xor(lsum[qt], 32) - masked;
-            if (row >= M) continue;
-            if (nsplit == 1) {
-                _Float16 *dst = o + ((size_t)b * M + row) * HD + 4 * h;
+            const int qr = 32 * qt + (lane & 31);
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) {
-                        half4 hv;
-#pragma unroll
-                        for (int y = 0; y < 4; ++y) hv[y] = (_Float16)(oacc[dt][qt][4 * rb + y] / l);
-                        *(half4 *)(dst + 32 * dt + 8 * rb) = hv;
-                    }
-            } else {
-                const size_t prow = ((size_t)split * B + b) * M + row;
-                float *dst = ws_w + prow * HD + 4 * h;
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb)
-                        *(float4v *)(dst + 32 * dt + 8 * rb) =
-                            float4v{oacc[dt][qt][4 * rb], oacc[dt][qt][4 * rb + 1], oacc[dt][qt][4 * rb + 2],
-                                    oacc[dt][qt][4 * rb + 3]};
-                if (h == 0) ws_l[prow] = l;
-            }
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int d = 32 * dt + 8 * rb + 4 * h;
+                    *(float4v *)(reg + qr * RED_ROW_BYTES + d * 4) =
+                        float4v{oacc[dt][qt][4 * rb], oacc[dt][qt][4 * rb + 1], oacc[dt][qt][4 * rb + 2],
+                                oacc[dt][qt][4 * rb + 3]};
+                }
+            const float mine = lsum[qt][0] + lsum[qt][1];
+            const float lfull = mine + __shfl_xor(mine, 32) - masked;
+            if (h == 0) lreg[qr] = lfull;
         }
-    } else {
-        // Sum the KS streams of each query group in LDS (fixed order), then
-        // write O (one split) or the partial W, L.
-        {
-            char *reg = smem + wave * C::RED_BYTES;
-            float *lreg = (float *)(reg + 32 * QT * RED_ROW_BYTES);
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                const int qr = 32 * qt + (lane & 31);
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) {
-                        const int d = 32 * dt + 8 * rb + 4 * h;
-                        *(float4v *)(reg + qr * RED_ROW_BYTES + d * 4) =
-                            float4v{oacc[dt][qt][4 * rb], oacc[dt][qt][4 * rb + 1], oacc[dt][qt][4 * rb + 2],
-                                    oacc[dt][qt][4 * rb + 3]};
-                    }
-                const float lfull = lsum[qt] + __shfl_xor(lsum[qt], 32) - masked;
-                if (h == 0) lreg[qr] = lfull;
-            }
-        }
-        __syncthreads();
-        if (qbase >= M) return;
+    }
+    __syncthreads();
+    {
         const int qr = lane % (32 * QT);
         const int d0 = ks * C::DW + (lane / (32 * QT)) * C::VPL;
         float acc[C::VPL];
@@ -542,6 +614,8 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const float *__restric
 template <int QT, int QW, int KS>
 int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
                        _Float16 *o, float *w, float *l, hipStream_t st) {
+    static_assert(32 * QT * QW == 32 || 32 * QT * QW == 64 || 32 * QT * QW == 128 || 32 * QT * QW == 256,
+                  "rows per workgroup");
     const int pairs = p.B * p.splits;
     const int groups = (pairs + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.mtiles));
@@ -555,8 +629,9 @@ int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k,
 namespace mga {
 
 static void ws_split(const Plan &p, const void *ws, float **w, float **l) {
+    const size_t rows = (size_t)p.splits * p.B * p.M;
     *w = (float *)ws;
-    *l = (float *)((char *)ws + (size_t)p.splits * p.B * p.M * HD * sizeof(float));
+    *l = (float *)((char *)ws + rows * HD * sizeof(float));
 }
 
 int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,

@@ -20,17 +20,9 @@ namespace mga {
 
 namespace {
 
-constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kTargetGroups = kCUs;  // one workgroup (4 waves, one per SIMD) per CU
+constexpr int kCUs = 256;  // MI355X compute units; one 8-wave workgroup fills one
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
-
-int variant_for(int M) {
-    if (M <= 32) return kVariantDecode;
-    if (M <= 64) return kVariantSmall;
-    if (M <= 128) return kVariantMedium;
-    return kVariantLarge;
-}
 
 int rows_for(int variant) {
     switch (variant) {
@@ -41,13 +33,25 @@ int rows_for(int variant) {
     }
 }
 
+// Query rows per workgroup: the largest tile whose workgroups alone (one
+// split) still cover every compute unit -- each K/V tile is then read by as
+// few workgroups as possible; with fewer rows than that, 64-row tiles (32
+// for M <= 32) and more splits, which keeps the per-workgroup K/V stream
+// short.
+int variant_for(int B, int M) {
+    if (M <= 32) return kVariantDecode;
+    if (M > 128 && (long long)B * ceil_div(M, 256) >= kCUs) return kVariantLarge;
+    if (M > 64 && (long long)B * ceil_div(M, 128) >= kCUs) return kVariantMedium;
+    return kVariantSmall;
+}
+
 // Policy: split the keys just enough that the grid reaches one workgroup per
 // compute unit; every split keeps at least one 128-key block.
-int policy_splits(int B, int M, int N) {
+int policy_splits(int B, int M, int N, int variant) {
     if (N < 1 || B < 1 || M < 1) return 1;
     const long long nblocks = ceil_div(N, kKeyBlock);
-    const long long base = (long long)B * ceil_div(M, rows_for(variant_for(M)));
-    const long long s = std::min(ceil_div(kTargetGroups, base), nblocks);
+    const long long base = (long long)B * ceil_div(M, rows_for(variant));
+    const long long s = std::min(ceil_div(kCUs, base), nblocks);
     return (int)std::max(1LL, s);
 }
 
@@ -63,11 +67,11 @@ int make_plan(int B, int M, int N, int splits, Plan *p) {
     p->B = B;
     p->M = M;
     p->N = N;
-    p->variant = variant_for(M);
+    p->variant = variant_for(B, M);
     p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;
-    const int want = splits == 0 ? policy_splits(B, M, N) : splits;
+    const int want = splits == 0 ? policy_splits(B, M, N, p->variant) : splits;
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);
@@ -169,6 +173,15 @@ int mga_gqa_forward(const void *q, const void *k, const void *v, void *o, int B,
     if (B == 0 || M == 0) return MGA_OK;
     if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
     if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
+    return MGA_OK;
+}
+
+int mga_gqa_plan(int B, int M, int N, int splits, int *tile_rows, int *eff_splits) {
+    mga::Plan p;
+    const int rc = mga::make_plan(B, M, N, splits, &p);
+    if (rc != MGA_OK) return rc;
+    if (tile_rows) *tile_rows = p.tile_rows;
+    if (eff_splits) *eff_splits = p.splits;
     return MGA_OK;
 }
 

@@ -19,10 +19,10 @@ struct Plan {
 
 // Kernel shapes: (query tiles of 32 per wave, query waves, key streams).
 // Every shape has 8 waves per workgroup (two per SIMD).
-constexpr int kVariantDecode = 0;  // M <= 32:  (1, 1, 8), 32 rows per workgroup
-constexpr int kVariantSmall = 1;   // M <= 64:  (2, 1, 8), 64 rows per workgroup
-constexpr int kVariantMedium = 2;  // M <= 128: (2, 2, 4), 128 rows per workgroup
-constexpr int kVariantLarge = 3;   // M > 128:  (2, 4, 2), 256 rows per workgroup
+constexpr int kVariantDecode = 0;  // (1, 1, 8),  32 rows per workgroup, wave-private rings
+constexpr int kVariantSmall = 1;   // (2, 1, 8),  64 rows per workgroup, wave-private rings
+constexpr int kVariantMedium = 2;  // (2, 2, 4), 128 rows per workgroup, shared ring
+constexpr int kVariantLarge = 3;   // (2, 4, 2), 256 rows per workgroup, shared ring
 
 constexpr int kKeyBlock = 128;
 // Buffer descriptors address one batch's K or V with 32-bit byte offsets.

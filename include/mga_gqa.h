@@ -28,11 +28,13 @@
  * multiple of 8 (every K row then starts on a 16-byte boundary).
  *
  * Numerics: fp16 MFMA products with fp32 accumulation; E = exp(A) in fp32
- * via the hardware exp2; the row-sum adds the fp32 E; P = fp16(E), rounded to
- * nearest even, feeds the second product. Results are deterministic for a
- * fixed (shape, splits): every sum runs in a fixed order and no atomics are
- * used. Inputs whose scores reach ln(65504) ~ 11.09 overflow fp16 P; results
- * are then undefined (the graph itself overflows there).
+ * via the hardware exp2 of log2(e) Q rounded to fp16; P = fp16(E), rounded to
+ * nearest even, is the tensor E of the fp16 graph: it feeds the second
+ * product and its fp32 row-sum is S, so numerator and denominator use the
+ * same weights. Results are deterministic for a fixed (shape, splits): every
+ * sum runs in a fixed order and no atomics are used. Inputs whose scores reach
+ * ln(65504) ~ 11.09 overflow fp16 P; results are then undefined (the graph
+ * itself overflows there).
  *
  * Ownership and asynchrony: the caller owns q, k, v, o and the workspace; the
  * library allocates and frees nothing on the device and keeps no device state,
@@ -87,9 +89,18 @@ int mga_gqa_choose_splits(int B, int M, int N);
 int mga_gqa_effective_splits(int B, int M, int N, int splits);
 
 /* Bytes of workspace mga_gqa_forward needs: 0 when the effective split count
- * is 1, else s*B*M*64*4 (fp32 numerators W[s][B][M][64]) + s*B*M*4 (fp32
- * denominators L[s][B][M]), rounded up to 256. Returns 0 for invalid shapes. */
+ * s is 1; else s*B*M*64*4 (fp32 numerators W[s][B][M][64]) + s*B*M*4 (fp32
+ * denominators L[s][B][M]), rounded up to 256. Its contents need no
+ * initialisation. Returns 0 for invalid shapes. */
 size_t mga_gqa_workspace_bytes(int B, int M, int N, int splits);
+
+/* The launch geometry the library picks (host only): query rows per
+ * workgroup (32, 64, 128 or 256: the largest tile whose workgroups still
+ * cover all 256 compute units without splitting, else 64, or 32 for M <= 32)
+ * and the effective split count. Either output pointer may be NULL. Returns
+ * the status mga_gqa_check_args would give for the shape (MGA_OK,
+ * INVALID_VALUE, LAYOUT or CONFIG). */
+int mga_gqa_plan(int B, int M, int N, int splits, int *tile_rows, int *eff_splits);
 
 /* Host-only validation of a forward call; makes no HIP call and launches
  * nothing, so it is usable without a GPU. Returns the status
@@ -101,7 +112,8 @@ int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *
 /* The whole path: partial kernel, then (when the effective split count is
  * above 1) the combine kernel, both on `stream`. splits = 0 lets the policy
  * choose. ws/ws_bytes: caller-owned device workspace of at least
- * mga_gqa_workspace_bytes(B, M, N, splits) bytes, 16-byte aligned. */
+ * mga_gqa_workspace_bytes(B, M, N, splits) bytes, 16-byte aligned. Calls
+ * that share a workspace must not overlap in time. */
 int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
                     int B, int M, int N, int splits, void *ws, size_t ws_bytes,
                     void *stream);

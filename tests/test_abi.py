@@ -98,11 +98,25 @@ def test_split_policy_and_workspace(B, M, N):
         assert 1 <= eff <= want
         assert (eff - 1) * chunk < nblocks          # no empty split
         ws = mga.mga_gqa_workspace_bytes(B, M, N, req)
+        rc, rows, eff2 = mga.mga_gqa_plan(B, M, N, req)
+        assert rc == mga.MGA_OK and eff2 == eff and rows in (32, 64, 128, 256)
         if eff == 1:
             assert ws == 0
         else:
             assert ws >= eff * B * M * 65 * 4 and ws % 256 == 0 and ws - eff * B * M * 65 * 4 < 256
     assert mga.mga_gqa_effective_splits(B, M, N, nblocks + 1) == -1
+    assert mga.mga_gqa_plan(B, M, N, nblocks + 1)[0] == mga.MGA_ERR_CONFIG
+
+
+@pytest.mark.parametrize("B,M,N,rows,splits", [
+    (16, 256, 4096, 64, 4),      # few query rows: 64-row tiles, 4 splits fill 256 CUs
+    (128, 256, 16384, 128, 1),   # 256 workgroups of 128 rows without splitting
+    (64, 8, 8192, 32, 4),        # decode-like rows: 32-row tiles
+    (2, 256, 32768, 64, 32),
+    (1024, 256, 1024, 256, 1),   # 256-row tiles already fill the chip
+])
+def test_plan_policy(B, M, N, rows, splits):
+    assert mga.mga_gqa_plan(B, M, N, 0) == (mga.MGA_OK, rows, splits)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

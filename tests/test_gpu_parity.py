@@ -177,6 +177,36 @@ def test_partial_then_combine_matches_forward(gpu):
         assert torch.equal(o, o_fwd)
 
 
+@pytest.mark.parametrize("B,M,N", [(16, 256, 4096), (64, 8, 8192), (3, 100, 1000), (128, 130, 520),
+                                   (256, 260, 136)])
+def test_partial_then_combine_each_tile_shape(gpu, B, M, N):
+    """Every query-tile shape the plan can pick (32, 64, 128 and 256 rows,
+    wave-private and shared rings): partial + combine equals forward bit for
+    bit, and a reused workspace gives the same bits on every call."""
+    import torch
+    q, k, v = make_qkv(B, M, N, seed=31, qk_std=0.3)
+    tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
+    nblocks = -(-N // mga.KEY_BLOCK)
+    stream = torch.cuda.current_stream()
+    for req in sorted({0, 2, 3, nblocks}):
+        if req > nblocks:
+            continue
+        rc, rows, s = mga.mga_gqa_plan(B, M, N, req)
+        assert rc == mga.MGA_OK
+        ws = mga.workspace_for(B, M, N, req, device=gpu)
+        nb = 0 if ws is None else ws.numel()
+        ref = torch.empty((B, M, 64), dtype=torch.float16, device=gpu)
+        assert mga.mga_gqa_partial(tq, tk, tv, ref, B, M, N, req, ws, nb, stream) == mga.MGA_OK
+        assert mga.mga_gqa_combine(ref, B, M, N, req, ws, nb, stream) == mga.MGA_OK
+        for call in range(3):
+            o = torch.full((B, M, 64), float("nan"), dtype=torch.float16, device=gpu)
+            assert mga.mga_gqa_forward(tq, tk, tv, o, B, M, N, req, ws, nb, stream) == mga.MGA_OK
+            torch.cuda.synchronize()
+            _say(f"[tile shapes] B={B} M={M} N={N} splits={s} rows={rows} call {call}")
+            assert torch.equal(o, ref), f"forward differs from partial+combine (call {call})"
+        assert_parity(ref.cpu().numpy(), oracle.gqa_f64(q, k, v), q, k, v, f"rows{rows} s{s}")
+
+
 def test_non_default_stream_and_empty_shapes(gpu):
     import torch
     q, k, v = make_qkv(2, 40, 520, seed=9)
