@@ -24,6 +24,10 @@ constexpr int kCUs = 256;  // MI355X compute units; one 8-wave workgroup fills o
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+constexpr long long kMinChunkBlocks = 4;
+// Most splits the policy uses for N keys.
+long long max_splits(int N) { return std::max(1LL, ceil_div(N, kKeyBlock) / kMinChunkBlocks); }
+
 int rows_for(int variant) {
     switch (variant) {
     case kVariantDecode: return 32;
@@ -33,25 +37,28 @@ int rows_for(int variant) {
     }
 }
 
-// Query rows per workgroup: the largest tile whose workgroups alone (one
-// split) still cover every compute unit -- each K/V tile is then read by as
-// few workgroups as possible; with fewer rows than that, 64-row tiles (32
-// for M <= 32) and more splits, which keeps the per-workgroup K/V stream
-// short.
-int variant_for(int B, int M) {
+// Query rows per workgroup. Larger tiles read each K/V tile into fewer
+// workgroups, but need enough (batch, query tile) pairs to cover the chip:
+// 256-row tiles when at most two key splits bring their grid to one
+// workgroup per compute unit, else 128-row tiles when they cover the chip
+// unsplit, else 64-row tiles (32 for M <= 32) and more key splits, which keep
+// each workgroup's K/V stream short.
+int variant_for(int B, int M, int N) {
     if (M <= 32) return kVariantDecode;
-    if (M > 128 && (long long)B * ceil_div(M, 256) >= kCUs) return kVariantLarge;
+    const long long two = std::min(2LL, max_splits(N));
+    if (M > 128 && (long long)B * ceil_div(M, 256) * two >= kCUs) return kVariantLarge;
     if (M > 64 && (long long)B * ceil_div(M, 128) >= kCUs) return kVariantMedium;
     return kVariantSmall;
 }
 
 // Policy: split the keys just enough that the grid reaches one workgroup per
-// compute unit; every split keeps at least one 128-key block.
+// compute unit, keeping at least kMinChunkBlocks key blocks per split where
+// N allows (shorter chunks cost more in partial traffic and combine work than
+// the extra workgroups gain).
 int policy_splits(int B, int M, int N, int variant) {
     if (N < 1 || B < 1 || M < 1) return 1;
-    const long long nblocks = ceil_div(N, kKeyBlock);
     const long long base = (long long)B * ceil_div(M, rows_for(variant));
-    const long long s = std::min(ceil_div(kCUs, base), nblocks);
+    const long long s = std::min(ceil_div(kCUs, base), max_splits(N));
     return (int)std::max(1LL, s);
 }
 
@@ -67,7 +74,7 @@ int make_plan(int B, int M, int N, int splits, Plan *p) {
     p->B = B;
     p->M = M;
     p->N = N;
-    p->variant = variant_for(B, M);
+    p->variant = variant_for(B, M, N);
     p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;

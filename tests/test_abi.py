@@ -110,9 +110,11 @@ def test_split_policy_and_workspace(B, M, N):
 
 @pytest.mark.parametrize("B,M,N,rows,splits", [
     (16, 256, 4096, 64, 4),      # few query rows: 64-row tiles, 4 splits fill 256 CUs
-    (128, 256, 16384, 128, 1),   # 256 workgroups of 128 rows without splitting
-    (64, 8, 8192, 32, 4),        # decode-like rows: 32-row tiles
+    (2, 256, 4096, 64, 8),       # 32 would fill the chip; chunks keep >= 4 key blocks
     (2, 256, 32768, 64, 32),
+    (64, 8, 8192, 32, 4),        # decode-like rows: 32-row tiles
+    (128, 256, 16384, 256, 2),   # 256-row tiles fill the chip with two splits
+    (128, 130, 520, 128, 1),     # 128-row tiles fill the chip unsplit
     (1024, 256, 1024, 256, 1),   # 256-row tiles already fill the chip
 ])
 def test_plan_policy(B, M, N, rows, splits):
