@@ -42,8 +42,9 @@
 //     three-phase software pipeline (first product of tile it, softmax of
 //     it-1, second product of it-2).
 // After the loop the KS streams of a query group are summed in LDS in a fixed
-// order; with one split the kernel writes O = fp16(W / L), otherwise W and L
-// go to the caller's workspace for the combine kernel.
+// order; with one split the kernel writes O = fp16(W / L), otherwise the
+// normalised partial o_s = fp16(W / L) and L go to the caller's workspace for
+// the combine kernel, which forms O = sum_s L_s o_s / sum_s L_s.
 //
 // Bounds. K/V/Q accesses go through buffer descriptors whose record count
 // ends at the last valid byte of batch b's array (or at zero for tiles past
@@ -333,7 +334,7 @@ __device__ __forceinline__ void pv(const half8 (&a)[2][2], const half8 (&p)[QT][
 template <int QT, int QW, int KS>
 __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const _Float16 *__restrict__ q, const _Float16 *__restrict__ k,
-    const _Float16 *__restrict__ v, _Float16 *__restrict__ o, float *__restrict__ ws_w,
+    const _Float16 *__restrict__ v, _Float16 *__restrict__ o, _Float16 *__restrict__ ws_o,
     float *__restrict__ ws_l, int B, int M, int N, int chunk_keys, int nsplit, int mtiles) {
     using C = Cfg<QT, QW, KS>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -577,19 +578,27 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                     *(half4 *)(dst + x) = hv;
                 }
             } else {
+                // Normalised partial: o_s = fp16(W_s / L_s), L_s in fp32 (0 when
+                // no weight survived fp16, so that it drops out of the combine).
                 const size_t prow = ((size_t)split * B + b) * M + row;
-                float *dst = ws_w + prow * HD + d0;
+                _Float16 *dst = ws_o + prow * HD + d0;
+                const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-                for (int x = 0; x < C::VPL; x += 4)
-                    *(float4v *)(dst + x) = float4v{acc[x], acc[x + 1], acc[x + 2], acc[x + 3]};
+                for (int x = 0; x < C::VPL; x += 4) {
+                    half4 hv;
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) hv[y] = (_Float16)(acc[x + y] * inv);
+                    *(half4 *)(dst + x) = hv;
+                }
                 if (ks == 0 && d0 == 0) ws_l[prow] = l;
             }
         }
     }
 }
 
-// Combine: 16 threads per output row, 4 head dims each; sums in split order.
-__global__ __launch_bounds__(256) void gqa_combine_kernel(const float *__restrict__ ws_w,
+// Combine: 16 threads per output row, 4 head dims each.
+// O = fp16(sum_s L_s o_s / sum_s L_s), both sums in split order.
+__global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__restrict__ ws_o,
                                                           const float *__restrict__ ws_l,
                                                           _Float16 *__restrict__ o, long long rows,
                                                           int nsplit) {
@@ -602,8 +611,11 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const float *__restric
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
         const long long prow = (long long)s * rows + row;
-        l += ws_l[prow];
-        acc += *reinterpret_cast<const float4v *>(ws_w + prow * HD + 4 * c);
+        const float ls = ws_l[prow];
+        const half4 os = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
+        l += ls;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += ls * (float)os[i];
     }
     half4 hv;
 #pragma unroll
@@ -613,7 +625,7 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const float *__restric
 
 template <int QT, int QW, int KS>
 int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
-                       _Float16 *o, float *w, float *l, hipStream_t st) {
+                       _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
     static_assert(32 * QT * QW == 32 || 32 * QT * QW == 64 || 32 * QT * QW == 128 || 32 * QT * QW == 256,
                   "rows per workgroup");
     const int pairs = p.B * p.splits;
@@ -628,15 +640,18 @@ int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k,
 
 namespace mga {
 
-static void ws_split(const Plan &p, const void *ws, float **w, float **l) {
+// Workspace: o_s [splits][B][M][64] fp16, then (from a 256-byte boundary)
+// L_s [splits][B][M] fp32.
+static void ws_split(const Plan &p, const void *ws, _Float16 **w, float **l) {
     const size_t rows = (size_t)p.splits * p.B * p.M;
-    *w = (float *)ws;
-    *l = (float *)((char *)ws + rows * HD * sizeof(float));
+    *w = (_Float16 *)ws;
+    *l = (float *)((char *)ws + ((rows * HD * sizeof(_Float16) + 255) & ~(size_t)255));
 }
 
 int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,
                    void *ws, void *stream) {
-    float *w = nullptr, *l = nullptr;
+    _Float16 *w = nullptr;
+    float *l = nullptr;
     if (p.splits > 1) ws_split(p, ws, &w, &l);
     hipStream_t st = (hipStream_t)stream;
     const _Float16 *qh = (const _Float16 *)q, *kh = (const _Float16 *)k, *vh = (const _Float16 *)v;
@@ -650,7 +665,8 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
 }
 
 int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
-    float *w = nullptr, *l = nullptr;
+    _Float16 *w = nullptr;
+    float *l = nullptr;
     ws_split(p, ws, &w, &l);
     const long long rows = (long long)p.B * p.M;
     const long long threads = rows * 16;

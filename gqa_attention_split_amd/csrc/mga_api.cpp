@@ -86,9 +86,10 @@ int make_plan(int B, int M, int N, int splits, Plan *p) {
     const long long groups = ceil_div((long long)B * p->splits, 8) * 8 * p->mtiles;
     if (groups > INT_MAX || (long long)B * M > INT_MAX / kHeadDim) return MGA_ERR_CONFIG;
     if (p->splits > 1) {
+        // o_s fp16 [splits][B][M][64] rounded up to 256 bytes, then L_s fp32 [splits][B][M]
         const size_t rows = (size_t)p->splits * B * M;
-        const size_t bytes = rows * kHeadDim * sizeof(float) + rows * sizeof(float);
-        p->ws_bytes = (bytes + 255) & ~(size_t)255;
+        const size_t o_bytes = (rows * kHeadDim * 2 + 255) & ~(size_t)255;
+        p->ws_bytes = (o_bytes + rows * sizeof(float) + 255) & ~(size_t)255;
     } else {
         p->ws_bytes = 0;
     }

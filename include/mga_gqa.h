@@ -16,8 +16,8 @@
  * the "attention" search configuration (a for-loop over the key dimension with
  * accumulation, then a combine across grid blocks). Because the graph
  * subtracts no running maximum, partials combine by plain sums:
- *     O = (sum_s W_s) / (sum_s L_s),  W_s = sum_{n in split s} e_n V[n],
- *                                     L_s = sum_{n in split s} e_n.
+ *     O = (sum_s L_s o_s) / (sum_s L_s),  o_s = W_s / L_s,
+ *     W_s = sum_{n in split s} e_n V[n],  L_s = sum_{n in split s} e_n.
  *
  * Data layout (all row-major, contiguous, IEEE fp16, device memory):
  *     q [B][M][64]     query rows (axis 0 = batch x KV heads)
@@ -31,7 +31,9 @@
  * via the hardware exp2 of log2(e) Q rounded to fp16; P = fp16(E), rounded to
  * nearest even, is the tensor E of the fp16 graph: it feeds the second
  * product and its fp32 row-sum is S, so numerator and denominator use the
- * same weights. Results are deterministic for a fixed (shape, splits): every
+ * same weights. With more than one split each partial o_s is stored rounded
+ * to fp16 (L_s stays fp32), which adds at most 2^-11 max_s |o_s| to the
+ * error. Results are deterministic for a fixed (shape, splits): every
  * sum runs in a fixed order and no atomics are used. Inputs whose scores reach
  * ln(65504) ~ 11.09 overflow fp16 P; results are then undefined (the graph
  * itself overflows there).
@@ -89,8 +91,9 @@ int mga_gqa_choose_splits(int B, int M, int N);
 int mga_gqa_effective_splits(int B, int M, int N, int splits);
 
 /* Bytes of workspace mga_gqa_forward needs: 0 when the effective split count
- * s is 1; else s*B*M*64*4 (fp32 numerators W[s][B][M][64]) + s*B*M*4 (fp32
- * denominators L[s][B][M]), rounded up to 256. Its contents need no
+ * s is 1; else the normalised partials o[s][B][M][64] in fp16 (s*B*M*128
+ * bytes, rounded up to 256) followed by the denominators L[s][B][M] in fp32
+ * (s*B*M*4 bytes), the total rounded up to 256. Its contents need no
  * initialisation. Returns 0 for invalid shapes. */
 size_t mga_gqa_workspace_bytes(int B, int M, int N, int splits);
 
@@ -120,14 +123,15 @@ int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
 
 /* Only the split-KV partial kernel (the for-loop over keys). With one
  * effective split it writes O directly (normalised, fp16); otherwise it
- * writes the partial numerators and denominators into `ws` and leaves `o`
+ * writes the normalised partials and denominators into `ws` and leaves `o`
  * untouched. Same arguments and checks as mga_gqa_forward. */
 int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
                     int B, int M, int N, int splits, void *ws, size_t ws_bytes,
                     void *stream);
 
-/* Only the combine kernel: O[b,i,:] = fp16(sum_s W[s,b,i,:] / sum_s L[s,b,i])
- * with the sums taken in split order. `ws` holds the partials a preceding
+/* Only the combine kernel:
+ *     O[b,i,:] = fp16(sum_s L[s,b,i] o[s,b,i,:] / sum_s L[s,b,i])
+ * with the sums taken in split order (fp32). `ws` holds the partials a preceding
  * mga_gqa_partial call wrote for the same (B, M, N, splits); q, k and v are
  * not read. A no-op returning MGA_OK when the effective split count is 1. */
 int mga_gqa_combine(void *o, int B, int M, int N, int splits,

@@ -103,7 +103,8 @@ def test_split_policy_and_workspace(B, M, N):
         if eff == 1:
             assert ws == 0
         else:
-            assert ws >= eff * B * M * 65 * 4 and ws % 256 == 0 and ws - eff * B * M * 65 * 4 < 256
+            o_bytes = -(-eff * B * M * 128 // 256) * 256     # fp16 partials, then fp32 denominators
+            assert ws == -(-(o_bytes + eff * B * M * 4) // 256) * 256
     assert mga.mga_gqa_effective_splits(B, M, N, nblocks + 1) == -1
     assert mga.mga_gqa_plan(B, M, N, nblocks + 1)[0] == mga.MGA_ERR_CONFIG
 

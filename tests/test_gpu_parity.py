@@ -177,12 +177,14 @@ def test_partial_then_combine_matches_forward(gpu):
         assert torch.equal(o, o_fwd)
 
 
-@pytest.mark.parametrize("B,M,N", [(16, 256, 4096), (64, 8, 8192), (3, 100, 1000), (128, 130, 520),
-                                   (256, 260, 136)])
+@pytest.mark.parametrize("B,M,N", [(16, 256, 4096), (64, 8, 8192), (3, 100, 1000),
+                                   (128, 130, 520), (128, 130, 264),     # 128-row tiles: refilled / resident ring
+                                   (256, 257, 520), (256, 260, 136)])    # 256-row tiles: refilled / resident ring
 def test_partial_then_combine_each_tile_shape(gpu, B, M, N):
     """Every query-tile shape the plan can pick (32, 64, 128 and 256 rows,
-    wave-private and shared rings): partial + combine equals forward bit for
-    bit, and a reused workspace gives the same bits on every call."""
+    wave-private and shared rings, the shared ring both refilled and with the
+    whole chunk resident): partial + combine equals forward bit for bit, and a
+    reused workspace gives the same bits on every call."""
     import torch
     q, k, v = make_qkv(B, M, N, seed=31, qk_std=0.3)
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
