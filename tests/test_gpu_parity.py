@@ -116,6 +116,56 @@ def test_small_and_ragged_shapes_all_splits(gpu, B, M, N):
         assert_parity(run_gpu(q, k, v, gpu, splits=s), ref, q, k, v, f"B{B} M{M} N{N} s{s}")
 
 
+def _quantized(shape, seed, scale):
+    """Seeded uniform inputs on a 1/256 grid (exact in fp16), cheap to draw in bulk."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.integers(-128, 128, size=shape, dtype=np.int8).astype(np.float16) * np.float16(scale))
+
+
+def test_largest_key_count(gpu):
+    """N at the top of the supported range (2^24 - 8): a batch's K and V byte
+    offsets reach 2^31, the per-lane K offsets d*N*2 their maximum, and the
+    last tile straddles N. Policy splits and one split per 128-key block."""
+    import torch
+    B, M, N = 1, 2, (1 << 24) - 8
+    q = _quantized((B, M, 64), 901, 1 / 256)            # |q| <= 0.5
+    k = _quantized((B, 64, N), 902, 1 / 512)            # |k| <= 0.25: |score| <= 64 * 0.5 * 0.25 = 8 < ln 65504
+    v = _quantized((B, N, 64), 903, 1 / 64)             # |v| <= 2
+    tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
+    ref = oracle.gqa_f64(q, k, v)
+    nblocks = -(-N // mga.KEY_BLOCK)
+    for s in (0, nblocks):
+        _say(f"[max N] B={B} M={M} N={N} splits={s} (effective {mga.mga_gqa_effective_splits(B, M, N, s)}, "
+             f"workspace {mga.mga_gqa_workspace_bytes(B, M, N, s)} B)")
+        o = mga.gqa_forward(tq, tk, tv, splits=s)
+        torch.cuda.synchronize()
+        assert_parity(o.cpu().numpy(), ref, q, k, v, f"max N s{s}")
+    del tq, tk, tv
+    torch.cuda.empty_cache()
+
+
+def test_many_query_rows(gpu):
+    """65536 batch rows x 256 queries (4 GiB of Q and of O) over 8 keys: row
+    and batch offsets past 2^31 elements' worth of bytes, a 65536-workgroup
+    grid; checked on sampled rows of every 4096th batch."""
+    import torch
+    B, M, N = 65536, 256, 8
+    q = _quantized((B, M, 64), 911, 1 / 256)
+    k = _quantized((B, 64, N), 912, 1 / 256)
+    v = _quantized((B, N, 64), 913, 1 / 64)
+    tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
+    _say(f"[many rows] B={B} M={M} N={N} plan={mga.mga_gqa_plan(B, M, N, 0)}")
+    o = mga.gqa_forward(tq, tk, tv).cpu().numpy()
+    torch.cuda.synchronize()
+    bs = np.arange(0, B, 4096).tolist() + [B - 1]
+    rows = sample_rows(M, 8, 5)
+    qs = np.ascontiguousarray(q[bs][:, rows])
+    ks, vs = np.ascontiguousarray(k[bs]), np.ascontiguousarray(v[bs])
+    assert_parity(o[bs][:, rows], oracle.gqa_f64(qs, ks, vs), qs, ks, vs, "many rows")
+    del tq, tk, tv
+    torch.cuda.empty_cache()
+
+
 def test_split_invariance_and_determinism(gpu):
     cfg = CONFIGS["gqa_b16_m256_n4096"]
     q, k, v = make_config(cfg)
