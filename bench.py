@@ -34,7 +34,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_FP16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gqa_partial_b16_m256_n4096.md")
 KERNEL_SRC = os.path.join(ROOT, "gqa_attention_split_amd", "csrc", "gqa_kernels.hip")
 
 
@@ -68,9 +67,11 @@ def kernel_source_sha() -> str:
 
 def read_traffic(config: str):
     """Counter-derived HBM bytes per partial-kernel launch, if the committed
-    counter summary was taken on the current kernel source; else None."""
+    counter summary for this workload was taken on the current kernel source;
+    else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gqa_partial_{config.replace('gqa_', '')}.md")
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
@@ -159,20 +160,20 @@ def main():
     from gqa_attention_split_amd.inputs import CONFIGS, make_config
 
     cfg = CONFIGS[args.config]
-    B, M, N = cfg.B, cfg.M, cfg.N
+    B, M, N, D = cfg.B, cfg.M, cfg.N, cfg.D
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(dev)  # default priority
 
     q, k, v = make_config(cfg)
-    set_bytes = q.nbytes + k.nbytes + v.nbytes + B * M * 64 * 2
+    set_bytes = q.nbytes + k.nbytes + v.nbytes + B * M * D * 2
     R = max(1, min(1024, math.ceil(args.rotate_bytes / set_bytes)))
     base = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
     sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
-    outs = [torch.empty((B, M, 64), dtype=torch.float16, device=dev) for _ in range(R)]
-    splits = args.splits if args.splits > 0 else mga.mga_gqa_choose_splits(B, M, N)
-    eff = mga.mga_gqa_effective_splits(B, M, N, splits)
-    ws = mga.workspace_for(B, M, N, splits, device=dev)
+    outs = [torch.empty((B, M, D), dtype=torch.float16, device=dev) for _ in range(R)]
+    splits = args.splits if args.splits > 0 else mga.mga_gqa_choose_splits(B, M, N, D)
+    eff = mga.mga_gqa_effective_splits(B, M, N, D, splits)
+    ws = mga.workspace_for(B, M, N, D, splits, device=dev)
     ws_ptr = 0 if ws is None else ws.data_ptr()
     ws_bytes = 0 if ws is None else ws.numel()
     lib = mga._lib.load()
@@ -183,24 +184,24 @@ def main():
 
     def fwd(i, rotate=True):
         j = i % R if rotate else 0
-        rc = lib.mga_gqa_forward(*ptrs[j], optr[j], B, M, N, splits, ws_ptr, ws_bytes, sh)
+        rc = lib.mga_gqa_forward(*ptrs[j], optr[j], B, M, N, D, splits, ws_ptr, ws_bytes, sh)
         if rc:
             raise mga.GqaError(rc)
 
     def partial(i, rotate=True):
         j = i % R if rotate else 0
-        rc = lib.mga_gqa_partial(*ptrs[j], optr[j], B, M, N, splits, ws_ptr, ws_bytes, sh)
+        rc = lib.mga_gqa_partial(*ptrs[j], optr[j], B, M, N, D, splits, ws_ptr, ws_bytes, sh)
         if rc:
             raise mga.GqaError(rc)
 
-    print(f"[bench] {cfg.name} B={B} M={M} N={N} splits={eff} rotating sets={R} "
+    print(f"[bench] {cfg.name} B={B} M={M} N={N} D={D} splits={eff} rotating sets={R} "
           f"({R * set_bytes / 2**20:.0f} MiB) steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
     gsteps = max(1, min(args.graph_steps, args.steps))
 
     def combine(i, rotate=True):
         j = i % R if rotate else 0
-        rc = lib.mga_gqa_combine(optr[j], B, M, N, splits, ws_ptr, ws_bytes, sh)
+        rc = lib.mga_gqa_combine(optr[j], B, M, N, D, splits, ws_ptr, ws_bytes, sh)
         if rc:
             raise mga.GqaError(rc)
 

@@ -1,9 +1,10 @@
 """Fused GQA exp-sum-div attention for MI355X (gfx950).
 
 Computes the Mirage GQA tutorial graph ("Mirage: Define GQA Computation
-Graph"): O = (E / rowsum(E)) V with E = exp(Q K), Q (B, M, 64), K stored
-head-dim-major as (B, 64, N), V (B, N, 64), all fp16, no scale and no max
-subtraction.
+Graph"): O = (E / rowsum(E)) V with E = exp(Q K), Q (B, M, D), K stored
+head-dim-major as (B, D, N), V (B, N, D), all fp16, no scale and no max
+subtraction. D is 64 (the tutorial graph) or 128 (the tutorial's launch
+example, Q (64, 1, 128)).
 
 The functions named ``mga_*`` mirror the C ABI in ``include/mga_gqa.h`` one to
 one and only marshal arguments (pointers may be ints or torch tensors; the
@@ -23,7 +24,7 @@ MGA_ERR_CONFIG = 3
 MGA_ERR_WORKSPACE = 4
 MGA_ERR_HIP = 5
 KEY_BLOCK = 128
-HEAD_DIM = 64
+HEAD_DIMS = (64, 128)
 
 
 class GqaError(RuntimeError):
@@ -53,43 +54,43 @@ def mga_status_string(status: int) -> str:
     return _lib.load().mga_status_string(int(status)).decode()
 
 
-def mga_gqa_choose_splits(B: int, M: int, N: int) -> int:
-    return _lib.load().mga_gqa_choose_splits(B, M, N)
+def mga_gqa_choose_splits(B: int, M: int, N: int, D: int) -> int:
+    return _lib.load().mga_gqa_choose_splits(B, M, N, D)
 
 
-def mga_gqa_effective_splits(B: int, M: int, N: int, splits: int) -> int:
-    return _lib.load().mga_gqa_effective_splits(B, M, N, splits)
+def mga_gqa_effective_splits(B: int, M: int, N: int, D: int, splits: int) -> int:
+    return _lib.load().mga_gqa_effective_splits(B, M, N, D, splits)
 
 
-def mga_gqa_workspace_bytes(B: int, M: int, N: int, splits: int) -> int:
-    return _lib.load().mga_gqa_workspace_bytes(B, M, N, splits)
+def mga_gqa_workspace_bytes(B: int, M: int, N: int, D: int, splits: int) -> int:
+    return _lib.load().mga_gqa_workspace_bytes(B, M, N, D, splits)
 
 
-def mga_gqa_plan(B: int, M: int, N: int, splits: int):
+def mga_gqa_plan(B: int, M: int, N: int, D: int, splits: int):
     """(status, tile_rows, effective_splits) for a shape."""
     import ctypes
     rows, eff = ctypes.c_int(0), ctypes.c_int(0)
-    rc = _lib.load().mga_gqa_plan(B, M, N, splits, ctypes.byref(rows), ctypes.byref(eff))
+    rc = _lib.load().mga_gqa_plan(B, M, N, D, splits, ctypes.byref(rows), ctypes.byref(eff))
     return rc, rows.value, eff.value
 
 
-def mga_gqa_check_args(q, k, v, o, B, M, N, splits, ws, ws_bytes) -> int:
-    return _lib.load().mga_gqa_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
+def mga_gqa_check_args(q, k, v, o, B, M, N, D, splits, ws, ws_bytes) -> int:
+    return _lib.load().mga_gqa_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D, splits,
                                           _ptr(ws), ws_bytes)
 
 
-def mga_gqa_forward(q, k, v, o, B, M, N, splits, ws, ws_bytes, stream) -> int:
-    return _lib.load().mga_gqa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
+def mga_gqa_forward(q, k, v, o, B, M, N, D, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D, splits,
                                        _ptr(ws), ws_bytes, _stream(stream))
 
 
-def mga_gqa_partial(q, k, v, o, B, M, N, splits, ws, ws_bytes, stream) -> int:
-    return _lib.load().mga_gqa_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, splits,
+def mga_gqa_partial(q, k, v, o, B, M, N, D, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D, splits,
                                        _ptr(ws), ws_bytes, _stream(stream))
 
 
-def mga_gqa_combine(o, B, M, N, splits, ws, ws_bytes, stream) -> int:
-    return _lib.load().mga_gqa_combine(_ptr(o), B, M, N, splits, _ptr(ws), ws_bytes,
+def mga_gqa_combine(o, B, M, N, D, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_combine(_ptr(o), B, M, N, D, splits, _ptr(ws), ws_bytes,
                                        _stream(stream))
 
 
@@ -106,42 +107,42 @@ def _check_tensors(q, k, v):
         if t.dim() != 3:
             raise ValueError(f"{name} must be 3-D")
     B, M, D = q.shape
-    if D != HEAD_DIM:
-        raise ValueError(f"head dim must be {HEAD_DIM}, got {D}")
+    if D not in HEAD_DIMS:
+        raise ValueError(f"head dim must be one of {HEAD_DIMS}, got {D}")
     if k.shape[0] != B or k.shape[1] != D:
-        raise ValueError(f"k must be (B, 64, N) = ({B}, 64, N), got {tuple(k.shape)}")
+        raise ValueError(f"k must be (B, D, N) = ({B}, {D}, N), got {tuple(k.shape)}")
     N = k.shape[2]
     if tuple(v.shape) != (B, N, D):
-        raise ValueError(f"v must be (B, N, 64) = ({B}, {N}, 64), got {tuple(v.shape)}")
+        raise ValueError(f"v must be (B, N, D) = ({B}, {N}, {D}), got {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
-    return B, M, N
+    return B, M, N, D
 
 
-def workspace_for(B: int, M: int, N: int, splits: int = 0, device=None):
+def workspace_for(B: int, M: int, N: int, D: int, splits: int = 0, device=None):
     """A torch uint8 workspace of mga_gqa_workspace_bytes(...) bytes (or None)."""
     import torch
-    nbytes = mga_gqa_workspace_bytes(B, M, N, splits)
+    nbytes = mga_gqa_workspace_bytes(B, M, N, D, splits)
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None):
-    """O = (exp(QK) / rowsum) V for fp16 CUDA tensors q (B,M,64), k (B,64,N), v (B,N,64)."""
+    """O = (exp(QK) / rowsum) V for fp16 GPU tensors q (B,M,D), k (B,D,N), v (B,N,D)."""
     import torch
-    B, M, N = _check_tensors(q, k, v)
+    B, M, N, D = _check_tensors(q, k, v)
     if out is None:
-        out = torch.empty((B, M, HEAD_DIM), dtype=torch.float16, device=q.device)
-    elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, HEAD_DIM) or \
+        out = torch.empty((B, M, D), dtype=torch.float16, device=q.device)
+    elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, D) or \
             not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous float16 (B, M, 64) tensor on q's device")
+        raise ValueError(f"out must be a contiguous float16 (B, M, {D}) tensor on q's device")
     if workspace is None:
-        workspace = workspace_for(B, M, N, splits, q.device)
+        workspace = workspace_for(B, M, N, D, splits, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = mga_gqa_forward(q, k, v, out, B, M, N, splits, workspace, ws_bytes, stream)
+    rc = mga_gqa_forward(q, k, v, out, B, M, N, D, splits, workspace, ws_bytes, stream)
     if rc != MGA_OK:
         raise GqaError(rc)
     return out

@@ -17,14 +17,14 @@ _I = ctypes.c_int
 _S = ctypes.c_size_t
 SIGNATURES = {
     "mga_status_string": ([_I], ctypes.c_char_p),
-    "mga_gqa_choose_splits": ([_I, _I, _I], _I),
-    "mga_gqa_effective_splits": ([_I, _I, _I, _I], _I),
-    "mga_gqa_workspace_bytes": ([_I, _I, _I, _I], _S),
-    "mga_gqa_plan": ([_I, _I, _I, _I, _P, _P], _I),
-    "mga_gqa_check_args": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _S], _I),
-    "mga_gqa_forward": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P], _I),
-    "mga_gqa_partial": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P], _I),
-    "mga_gqa_combine": ([_P, _I, _I, _I, _I, _P, _S, _P], _I),
+    "mga_gqa_choose_splits": ([_I, _I, _I, _I], _I),
+    "mga_gqa_effective_splits": ([_I, _I, _I, _I, _I], _I),
+    "mga_gqa_workspace_bytes": ([_I, _I, _I, _I, _I], _S),
+    "mga_gqa_plan": ([_I, _I, _I, _I, _I, _P, _P], _I),
+    "mga_gqa_check_args": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S], _I),
+    "mga_gqa_forward": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
+    "mga_gqa_partial": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
+    "mga_gqa_combine": ([_P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
 }
 
 _lib = None

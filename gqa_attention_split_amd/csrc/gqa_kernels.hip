@@ -73,14 +73,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
 
-constexpr int HD = mga::kHeadDim;            // 64
 constexpr int KT = 32;                       // keys per tile
-constexpr int TILE_BYTES = KT * HD * 2 * 2;  // K part 4 KiB + V part 4 KiB
-constexpr int K_ROW_BYTES = KT * 2;          // 64
-constexpr int V_ROW_BYTES = HD * 2;          // 128
-constexpr int V_PART = KT * HD * 2;          // byte offset of the V part in a tile
-constexpr int Q_ROW_BYTES = HD * 2;          // 128
-constexpr int RED_ROW_BYTES = HD * 4 + 16;   // fp32 row of 64 + 16-byte pad (bank spread)
+constexpr int K_ROW_BYTES = KT * 2;          // 64: one head dim's 32 keys
 constexpr int LDS_LIMIT = 160 * 1024;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int BUFFER_FLAGS = 0x00020000;     // gfx9 raw buffer descriptor, dword 3
@@ -88,6 +82,24 @@ constexpr uint32_t OOB = 0x80000000u;        // offset past every descriptor's r
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Tile geometry for head dim HD (64 or 128). A tile is 32 keys: the K part
+// [HD d][32 keys] (64-byte rows) followed by the V part [32 keys][HD d].
+template <int HD>
+struct Geo {
+    static_assert(HD == 64 || HD == 128, "head dim");
+    static constexpr int V_ROW_BYTES = HD * 2;
+    static constexpr int V_PART = KT * HD * 2;        // byte offset of the V part in a tile
+    static constexpr int TILE_BYTES = 2 * V_PART;     // 8 KiB (HD 64) or 16 KiB (HD 128)
+    static constexpr int Q_ROW_BYTES = HD * 2;
+    static constexpr int RED_ROW_BYTES = HD * 4 + 16;  // fp32 row + 16-byte pad (bank spread)
+    static constexpr int KSTEPS = HD / 16;            // 16-deep k-steps of the first product
+    static constexpr int DT = HD / 32;                // 32-row blocks of O^T
+    static constexpr int DMA = HD / 16;               // 1 KiB DMA instructions per tile part
+    static constexpr int V_LPR = HD / 8;              // lanes per V row (16 bytes each)
+    static constexpr int V_RPI = 64 / V_LPR;          // V rows per DMA instruction
+    static_assert(V_RPI % 4 == 0, "V swizzle needs whole groups of four rows per instruction");
+};
 
 __device__ __forceinline__ half8 cat8(fp16x4 lo, fp16x4 hi) {
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
@@ -103,19 +115,23 @@ __device__ __forceinline__ fp16x4 tr_read(const char *lds_byte_addr) {
 __device__ __forceinline__ int k_off(int d, int col_byte) {
     return d * K_ROW_BYTES + (((col_byte >> 5) ^ ((d >> 1) & 1)) << 5) + (col_byte & 31);
 }
-// V part: [32 keys][64 d] fp16, 128-byte rows of four 32-byte units; the unit
-// index is XORed with the row's low two bits.
+// V part: [32 keys][HD d] fp16, rows of HD/16 32-byte units; the unit index
+// is XORed with the row's low two bits.
+template <int HD>
 __device__ __forceinline__ int v_off(int key, int col_byte) {
-    return V_PART + key * V_ROW_BYTES + (((col_byte >> 5) ^ (key & 3)) << 5) + (col_byte & 31);
+    using G = Geo<HD>;
+    return G::V_PART + key * G::V_ROW_BYTES + (((col_byte >> 5) ^ (key & 3)) << 5) + (col_byte & 31);
 }
 
-template <int QT, int QW, int KS>
+template <int HD, int QT, int QW, int KS>
 struct Cfg {
+    using G = Geo<HD>;
+    static constexpr int TILE_BYTES = G::TILE_BYTES;
     static constexpr int NWAVES = QW * KS;
     static constexpr int ROWS = 32 * QT * QW;   // query rows per workgroup
-    static_assert(4 % QW == 0, "QW must divide the 4 K and 4 V DMA instructions of a tile");
+    static_assert(G::DMA % QW == 0, "QW must divide the K and V DMA instructions of a tile");
     static_assert(KS >= 2, "streams");
-    static constexpr int PER = 4 / QW;          // K (and V) DMA instructions per wave per tile
+    static constexpr int PER = G::DMA / QW;     // K (and V) DMA instructions per wave per tile
     static constexpr int TILE_OPS = 2 * PER;    // DMA instructions per wave per tile
     static constexpr bool PRIVATE = QW == 1;
     // Shared ring: each buffer holds one tile per stream; step `it` refills
@@ -126,10 +142,10 @@ struct Cfg {
     static constexpr int RING_BYTES = PRIVATE ? NWAVES * 2 * TILE_BYTES : STAGES * STAGE_BYTES;
     // Q staging: past the private rings, or in shared-ring buffers that the
     // prologue leaves empty (DIST .. STAGES-1).
-    static constexpr int Q_BYTES = ROWS * Q_ROW_BYTES;
+    static constexpr int Q_BYTES = ROWS * G::Q_ROW_BYTES;
     static constexpr int Q_OFF = PRIVATE ? RING_BYTES : DIST * STAGE_BYTES;
-    static constexpr int Q_OPS = ROWS / 8;      // 1 KiB DMA instructions for the workgroup's Q
-    static constexpr int RED_BYTES = 32 * QT * RED_ROW_BYTES + 32 * QT * 4;  // one wave's epilogue region
+    static constexpr int Q_OPS = Q_BYTES / 1024;  // 1 KiB DMA instructions for the workgroup's Q
+    static constexpr int RED_BYTES = 32 * QT * G::RED_ROW_BYTES + 32 * QT * 4;  // one wave's epilogue region
     static constexpr int LDS_BYTES = cmax(cmax(RING_BYTES, Q_OFF + Q_BYTES), NWAVES * RED_BYTES);
     static constexpr int DW = HD / KS;                // head dims each wave finalises
     static constexpr int VPL = 32 * QT * DW / 64;     // values per lane in the final write
@@ -182,19 +198,21 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // Per-lane DMA offsets of this wave's share of a tile (independent of the
 // tile's position: the descriptor base moves instead). K instruction x fills
 // K rows 16 r .. 16 r + 15 (r = qw*PER + x), 4 lanes per 64-byte row; V
-// instruction x fills V rows 8 r .. 8 r + 7, 8 lanes per 128-byte row. A lane
-// fetches the 16-byte unit that the row's swizzle puts at its position.
-template <int QW>
+// instruction x fills V rows V_RPI r .. V_RPI (r + 1) - 1, V_LPR lanes per
+// row. A lane fetches the 16-byte unit that the row's swizzle puts at its
+// position.
+template <int HD, int QW>
 struct TileDma {
-    static constexpr int PER = 4 / QW;
+    static constexpr int PER = Geo<HD>::DMA / QW;
     uint32_t koff[PER];  // byte offset of the lane's 8 keys of head dim d from the tile's key 0
     uint32_t kcol;       // first key of those 8, relative to the tile start
-    uint32_t voff;       // byte offset within the tile's 32 x 64 V block (instruction 0)
+    uint32_t voff;       // byte offset within the tile's 32 x HD V block (instruction 0)
 };
-template <int QW>
-__device__ __forceinline__ TileDma<QW> make_tile_dma(int qw, int lane, int N) {
-    constexpr int PER = 4 / QW;
-    TileDma<QW> t;
+template <int HD, int QW>
+__device__ __forceinline__ TileDma<HD, QW> make_tile_dma(int qw, int lane, int N) {
+    using G = Geo<HD>;
+    constexpr int PER = G::DMA / QW;
+    TileDma<HD, QW> t;
     const uint32_t lc = (lane & 3) ^ (((lane >> 3) & 1) << 1);  // bit 1 of d = bit 3 of lane
     t.kcol = 8 * lc;
 #pragma unroll
@@ -202,8 +220,8 @@ __device__ __forceinline__ TileDma<QW> make_tile_dma(int qw, int lane, int N) {
         const uint32_t d = 16 * (qw * PER + x) + (lane >> 2);
         t.koff[x] = (d * (uint32_t)N + t.kcol) * 2;
     }
-    const uint32_t kr = 8 * (qw * PER) + (lane >> 3);
-    const uint32_t vc = (lane & 7) ^ ((kr & 3) << 1);
+    const uint32_t kr = G::V_RPI * (qw * PER) + lane / G::V_LPR;
+    const uint32_t vc = (lane % G::V_LPR) ^ ((kr & 3) << 1);
     t.voff = (kr * HD + 8 * vc) * 2;
     return t;
 }
@@ -213,10 +231,10 @@ __device__ __forceinline__ TileDma<QW> make_tile_dma(int qw, int lane, int N) {
 // byte address `lds`. `live` is false for tiles past the chunk end: their
 // descriptors hold zero records and the tile fills with zeros without
 // touching memory. The descriptors start at the tile and end with the batch.
-template <int QW>
+template <int HD, int QW>
 __device__ __forceinline__ void issue_tile(const _Float16 *kb, const _Float16 *vb, int N, int key0,
-                                           bool live, uint32_t lds, int qw, const TileDma<QW> &t) {
-    constexpr int PER = 4 / QW;
+                                           bool live, uint32_t lds, int qw, const TileDma<HD, QW> &t) {
+    constexpr int PER = Geo<HD>::DMA / QW;
     const int rem = N - key0;  // keys from key0 to the end of the batch (> 0 when live)
     const i32x4 kr = make_rsrc(kb + key0, live ? (uint32_t)(HD * N - key0) * 2 : 0u);
     const i32x4 vr = make_rsrc(vb + (size_t)key0 * HD, live ? (uint32_t)rem * (HD * 2) : 0u);
@@ -224,7 +242,7 @@ __device__ __forceinline__ void issue_tile(const _Float16 *kb, const _Float16 *v
 #pragma unroll
     for (int x = 0; x < PER; ++x) dma16(kr, kin ? t.koff[x] : OOB, lds + (qw * PER + x) * 1024);
 #pragma unroll
-    for (int x = 0; x < PER; ++x) dma16(vr, t.voff + x * 1024, lds + V_PART + (qw * PER + x) * 1024);
+    for (int x = 0; x < PER; ++x) dma16(vr, t.voff + x * 1024, lds + Geo<HD>::V_PART + (qw * PER + x) * 1024);
 }
 
 // Keys of a chunk of `len` keys that fall into this stream's first `nt` tiles
@@ -252,44 +270,48 @@ __device__ __forceinline__ int opaque(int x) {
 // steps leave unchanged, and the V part's on the row's low two bits, which
 // the +8 and +16 row steps leave unchanged; so one base per read family
 // plus immediate offsets covers every read.
+template <int HD>
 struct LaneOffsets {
-    int k;      // K part, head dims 8h+jr (+4, +16 kk), keys 16 g1 + 4c
-    int v[2];   // V part, keys 4h+jr (+8, +16 t), head dims 32 dt + 16 g1 + 4c
+    int k;                // K part, head dims 8h+jr (+4, +16 kk), keys 16 g1 + 4c
+    int v[Geo<HD>::DT];   // V part, keys 4h+jr (+8, +16 t), head dims 32 dt + 16 g1 + 4c
 };
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+template <int HD>
+__device__ __forceinline__ LaneOffsets<HD> lane_offsets(int lane) {
     const int h = lane >> 5, g1 = (lane >> 4) & 1, jr = (lane & 15) >> 2, cb = 8 * (lane & 3);
-    LaneOffsets r;
+    LaneOffsets<HD> r;
     r.k = k_off(8 * h + jr, 32 * g1 + cb);
-    r.v[0] = v_off(4 * h + jr, 32 * g1 + cb);
-    r.v[1] = v_off(4 * h + jr, 64 + 32 * g1 + cb);
+#pragma unroll
+    for (int dt = 0; dt < Geo<HD>::DT; ++dt) r.v[dt] = v_off<HD>(4 * h + jr, 64 * dt + 32 * g1 + cb);
     return r;
 }
 
-// A operands of the first product (K^T, four 16-deep k-steps) and of the
+// A operands of the first product (K^T, HD/16 k-steps of 16) and of the
 // second product (V^T: [t][dt] = keys 16t.., head dims 32dt..).
-__device__ __forceinline__ void read_k(const char *kb, half8 (&a)[4]) {
+template <int HD>
+__device__ __forceinline__ void read_k(const char *kb, half8 (&a)[Geo<HD>::KSTEPS]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < Geo<HD>::KSTEPS; ++kk)
         a[kk] = cat8(tr_read(kb + kk * 16 * K_ROW_BYTES), tr_read(kb + kk * 16 * K_ROW_BYTES + 4 * K_ROW_BYTES));
 }
-__device__ __forceinline__ void read_v(const char *vb0, const char *vb1, half8 (&a)[2][2]) {
+template <int HD>
+__device__ __forceinline__ void read_v(const char *const (&vb)[Geo<HD>::DT], half8 (&a)[2][Geo<HD>::DT]) {
+    constexpr int VR = Geo<HD>::V_ROW_BYTES;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            const char *vb = (dt == 0 ? vb0 : vb1) + t * 16 * V_ROW_BYTES;
-            a[t][dt] = cat8(tr_read(vb), tr_read(vb + 8 * V_ROW_BYTES));
-        }
+        for (int dt = 0; dt < Geo<HD>::DT; ++dt)
+            a[t][dt] = cat8(tr_read(vb[dt] + t * 16 * VR), tr_read(vb[dt] + t * 16 * VR + 8 * VR));
 }
 
 // First product of one tile for one wave (32*QT queries): S^T = K^T Q^T.
-template <int QT>
-__device__ __forceinline__ void scores(const half8 (&a)[4], const half8 (&qf)[QT][4], float16v (&s)[QT]) {
+template <int HD, int QT>
+__device__ __forceinline__ void scores(const half8 (&a)[Geo<HD>::KSTEPS],
+                                       const half8 (&qf)[QT][Geo<HD>::KSTEPS], float16v (&s)[QT]) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         s[qt] = float16v{};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < Geo<HD>::KSTEPS; ++kk)
             s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[kk], qf[qt][kk], s[qt], 0, 0, 0);
     }
 }
@@ -320,23 +342,26 @@ __device__ __forceinline__ void softmax(const float16v (&s)[QT], half8 (&p)[QT][
 }
 
 // Second product of one tile: O^T += V^T P^T.
-template <int QT>
-__device__ __forceinline__ void pv(const half8 (&a)[2][2], const half8 (&p)[QT][2], float16v (&oacc)[2][QT]) {
+template <int HD, int QT>
+__device__ __forceinline__ void pv(const half8 (&a)[2][Geo<HD>::DT], const half8 (&p)[QT][2],
+                                   float16v (&oacc)[Geo<HD>::DT][QT]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < Geo<HD>::DT; ++dt)
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
                 oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t][dt], p[qt][t], oacc[dt][qt], 0, 0, 0);
 }
 
-template <int QT, int QW, int KS>
+template <int HD, int QT, int QW, int KS>
 __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const _Float16 *__restrict__ q, const _Float16 *__restrict__ k,
     const _Float16 *__restrict__ v, _Float16 *__restrict__ o, _Float16 *__restrict__ ws_o,
     float *__restrict__ ws_l, int B, int M, int N, int chunk_keys, int nsplit, int mtiles) {
-    using C = Cfg<QT, QW, KS>;
+    using C = Cfg<HD, QT, QW, KS>;
+    using G = Geo<HD>;
+    constexpr int TILE_BYTES = G::TILE_BYTES, DT = G::DT, KSTEPS = G::KSTEPS;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     // Workgroup -> (batch, split, query tile). Consecutive workgroup ids go to
@@ -358,12 +383,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const int qrow0 = mtile * C::ROWS;                     // first query row of the workgroup
     const int qbase = qrow0 + qw * 32 * QT;                // first query row of this wave
 
-    const _Float16 *kb = k + (size_t)b * HD * N;  // batch b's K [64][N] and V [N][64]
+    const _Float16 *kb = k + (size_t)b * HD * N;  // batch b's K [HD][N] and V [N][HD]
     const _Float16 *vb = v + (size_t)b * N * HD;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)(smem));
-    const LaneOffsets lo = lane_offsets(lane);
-    const TileDma<QW> td = make_tile_dma<QW>(qw, lane, N);
+    const LaneOffsets<HD> lo = lane_offsets<HD>(lane);
+    const TileDma<HD, QW> td = make_tile_dma<HD, QW>(qw, lane, N);
 
     // Tiles are numbered per stream: tile it of stream ks starts at chunk key
     // (it*KS + ks)*32. `ntiles` counts the tiles a stream visits.
@@ -372,28 +397,28 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                                   : (len + KS * KT - 1) / (KS * KT);
     auto tile_key = [&](int it) { return (it * KS + ks) * KT; };  // relative to kstart
     auto issue = [&](int it, uint32_t lds) {
-        issue_tile<QW>(kb, vb, N, kstart + tile_key(it), it < ntiles && tile_key(it) < len, lds, qw, td);
+        issue_tile<HD, QW>(kb, vb, N, kstart + tile_key(it), it < ntiles && tile_key(it) < len, lds, qw, td);
     };
 
     // Q for the workgroup's rows -> LDS (rows past M read zero). Issued before
     // any K/V tile so that the first step finds it.
     {
         const int qrows = min(C::ROWS, M - qrow0);
-        const i32x4 qr = make_rsrc(q + ((size_t)b * M + qrow0) * HD, (uint32_t)qrows * Q_ROW_BYTES);
+        const i32x4 qr = make_rsrc(q + ((size_t)b * M + qrow0) * HD, (uint32_t)qrows * G::Q_ROW_BYTES);
         for (int j = wave; j < C::Q_OPS; j += C::NWAVES)
             dma16(qr, (uint32_t)(j * 1024 + lane * 16), lds0 + C::Q_OFF + j * 1024);
     }
 
-    float16v oacc[2][QT];
+    float16v oacc[DT][QT];
     float lsum[QT][2];  // per lane: its 16 keys of every tile, two chains
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-        oacc[0][qt] = float16v{};
-        oacc[1][qt] = float16v{};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = float16v{};
         lsum[qt][0] = 0.f;
         lsum[qt][1] = 0.f;
     }
-    half8 qf[QT][4];
+    half8 qf[QT][KSTEPS];
     // Q^T fragments (B operand): lane holds query qbase + 32*qt + (lane & 31),
     // head dims 16*kk + 8*h .. +7, pre-scaled by log2(e) (fp32 product rounded
     // to fp16) so that the first product yields log2-domain scores and
@@ -401,9 +426,9 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     auto load_q = [&]() {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-            const char *row = smem + C::Q_OFF + (qbase - qrow0 + 32 * qt + (lane & 31)) * Q_ROW_BYTES + 16 * h;
+            const char *row = smem + C::Q_OFF + (qbase - qrow0 + 32 * qt + (lane & 31)) * G::Q_ROW_BYTES + 16 * h;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < KSTEPS; ++kk) {
                 half8 x = *reinterpret_cast<const half8 *>(row + 32 * kk);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = (_Float16)((float)x[j] * LOG2E);
@@ -424,16 +449,19 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         for (int it = 0; it < ntiles; ++it) {
             wait_vm<C::TILE_OPS>();  // tile it landed (tile it+1 may still be in flight)
             const char *buf = ring + (it & 1) * TILE_BYTES;
-            half8 ka[4], va[2][2];
-            read_k(buf + lo.k, ka);
-            read_v(buf + lo.v[0], buf + lo.v[1], va);
+            half8 ka[KSTEPS], va[2][DT];
+            const char *vbase[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vbase[dt] = buf + lo.v[dt];
+            read_k<HD>(buf + lo.k, ka);
+            read_v<HD>(vbase, va);
             wait_lds();              // the buffer is free: refill it with tile it+2
             issue(it + 2, ring0 + (it & 1) * TILE_BYTES);
             float16v s[QT];
             half8 p[QT][2];
-            scores<QT>(ka, qf, s);
+            scores<HD, QT>(ka, qf, s);
             softmax<QT>(s, p, lsum);
-            pv<QT>(va, p, oacc);
+            pv<HD, QT>(va, p, oacc);
         }
         wait_vm<0>();
         __syncthreads();  // every ring and the Q staging are free for the reduction
@@ -468,15 +496,18 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         float16v s0[QT], s1[QT];
         half8 p[QT][2];
         auto g1 = [&](int it, float16v (&sv)[QT]) {
-            half8 a[4];
-            read_k(tile_at(it) + opaque(lo.k), a);
-            scores<QT>(a, qf, sv);
+            half8 a[KSTEPS];
+            read_k<HD>(tile_at(it) + opaque(lo.k), a);
+            scores<HD, QT>(a, qf, sv);
         };
         auto sm = [&](const float16v (&sv)[QT]) { softmax<QT>(sv, p, lsum); };
         auto g2 = [&](int it) {
-            half8 a[2][2];
-            read_v(tile_at(it) + opaque(lo.v[0]), tile_at(it) + opaque(lo.v[1]), a);
-            pv<QT>(a, p, oacc);
+            half8 a[2][DT];
+            const char *vbase[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vbase[dt] = tile_at(it) + opaque(lo.v[dt]);
+            read_v<HD>(vbase, a);
+            pv<HD, QT>(a, p, oacc);
         };
         const int niter = ntiles;
         sync();                 // step 0
@@ -526,16 +557,16 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     // write O (one split) or the partial W, L.
     {
         char *reg = smem + wave * C::RED_BYTES;
-        float *lreg = (float *)(reg + 32 * QT * RED_ROW_BYTES);
+        float *lreg = (float *)(reg + 32 * QT * G::RED_ROW_BYTES);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const int qr = 32 * qt + (lane & 31);
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const int d = 32 * dt + 8 * rb + 4 * h;
-                    *(float4v *)(reg + qr * RED_ROW_BYTES + d * 4) =
+                    *(float4v *)(reg + qr * G::RED_ROW_BYTES + d * 4) =
                         float4v{oacc[dt][qt][4 * rb], oacc[dt][qt][4 * rb + 1], oacc[dt][qt][4 * rb + 2],
                                 oacc[dt][qt][4 * rb + 3]};
                 }
@@ -555,10 +586,10 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
             const char *reg = smem + (qw * KS + s2) * C::RED_BYTES;
-            const float *lreg = (const float *)(reg + 32 * QT * RED_ROW_BYTES);
+            const float *lreg = (const float *)(reg + 32 * QT * G::RED_ROW_BYTES);
 #pragma unroll
             for (int x = 0; x < C::VPL; x += 4) {
-                const float4v t = *(const float4v *)(reg + qr * RED_ROW_BYTES + (d0 + x) * 4);
+                const float4v t = *(const float4v *)(reg + qr * G::RED_ROW_BYTES + (d0 + x) * 4);
                 acc[x] += t[0];
                 acc[x + 1] += t[1];
                 acc[x + 2] += t[2];
@@ -596,15 +627,16 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     }
 }
 
-// Combine: 16 threads per output row, 4 head dims each.
+// Combine: HD/4 threads per output row, 4 head dims each.
 // O = fp16(sum_s L_s o_s / sum_s L_s), both sums in split order.
+template <int HD>
 __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__restrict__ ws_o,
                                                           const float *__restrict__ ws_l,
                                                           _Float16 *__restrict__ o, long long rows,
                                                           int nsplit) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long row = gid >> 4;
-    const int c = (int)(gid & 15);
+    const long long row = gid / (HD / 4);
+    const int c = (int)(gid % (HD / 4));
     if (row >= rows) return;
     float l = 0.f;
     float4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -623,7 +655,7 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     *reinterpret_cast<half4 *>(o + row * HD + 4 * c) = hv;
 }
 
-template <int QT, int QW, int KS>
+template <int HD, int QT, int QW, int KS>
 int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
                        _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
     static_assert(32 * QT * QW == 32 || 32 * QT * QW == 64 || 32 * QT * QW == 128 || 32 * QT * QW == 256,
@@ -631,7 +663,7 @@ int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k,
     const int pairs = p.B * p.splits;
     const int groups = (pairs + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.mtiles));
-    hipLaunchKernelGGL((gqa_partial_kernel<QT, QW, KS>), grid, dim3(64 * QW * KS), 0, st, q, k, v, o,
+    hipLaunchKernelGGL((gqa_partial_kernel<HD, QT, QW, KS>), grid, dim3(64 * QW * KS), 0, st, q, k, v, o,
                        w, l, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles);
     return (int)hipGetLastError();
 }
@@ -640,12 +672,12 @@ int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k,
 
 namespace mga {
 
-// Workspace: o_s [splits][B][M][64] fp16, then (from a 256-byte boundary)
+// Workspace: o_s [splits][B][M][D] fp16, then (from a 256-byte boundary)
 // L_s [splits][B][M] fp32.
 static void ws_split(const Plan &p, const void *ws, _Float16 **w, float **l) {
     const size_t rows = (size_t)p.splits * p.B * p.M;
     *w = (_Float16 *)ws;
-    *l = (float *)((char *)ws + ((rows * HD * sizeof(_Float16) + 255) & ~(size_t)255));
+    *l = (float *)((char *)ws + ((rows * p.D * sizeof(_Float16) + 255) & ~(size_t)255));
 }
 
 int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,
@@ -657,10 +689,12 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
     const _Float16 *qh = (const _Float16 *)q, *kh = (const _Float16 *)k, *vh = (const _Float16 *)v;
     _Float16 *oh = (_Float16 *)o;
     switch (p.variant) {
-    case kVariantDecode: return launch_partial_cfg<1, 1, 8>(p, qh, kh, vh, oh, w, l, st);
-    case kVariantSmall: return launch_partial_cfg<2, 1, 8>(p, qh, kh, vh, oh, w, l, st);
-    case kVariantMedium: return launch_partial_cfg<2, 2, 4>(p, qh, kh, vh, oh, w, l, st);
-    default: return launch_partial_cfg<2, 4, 2>(p, qh, kh, vh, oh, w, l, st);
+    case kVariantDecode: return launch_partial_cfg<64, 1, 1, 8>(p, qh, kh, vh, oh, w, l, st);
+    case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8>(p, qh, kh, vh, oh, w, l, st);
+    case kVariantMedium: return launch_partial_cfg<64, 2, 2, 4>(p, qh, kh, vh, oh, w, l, st);
+    case kVariantLarge: return launch_partial_cfg<64, 2, 4, 2>(p, qh, kh, vh, oh, w, l, st);
+    case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4>(p, qh, kh, vh, oh, w, l, st);
+    default: return (int)hipErrorInvalidValue;
     }
 }
 
@@ -669,10 +703,14 @@ int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
     float *l = nullptr;
     ws_split(p, ws, &w, &l);
     const long long rows = (long long)p.B * p.M;
-    const long long threads = rows * 16;
+    const long long threads = rows * (p.D / 4);
     const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(gqa_combine_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
-                       (_Float16 *)o, rows, p.splits);
+    if (p.D == 128)
+        hipLaunchKernelGGL(gqa_combine_kernel<128>, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
+                           (_Float16 *)o, rows, p.splits);
+    else
+        hipLaunchKernelGGL(gqa_combine_kernel<64>, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
+                           (_Float16 *)o, rows, p.splits);
     return (int)hipGetLastError();
 }
 

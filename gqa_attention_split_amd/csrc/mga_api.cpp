@@ -30,7 +30,8 @@ long long max_splits(int N) { return std::max(1LL, ceil_div(N, kKeyBlock) / kMin
 
 int rows_for(int variant) {
     switch (variant) {
-    case kVariantDecode: return 32;
+    case kVariantDecode:
+    case kVariantDecode128: return 32;
     case kVariantSmall: return 64;
     case kVariantMedium: return 128;
     default: return 256;
@@ -43,7 +44,8 @@ int rows_for(int variant) {
 // workgroup per compute unit, else 128-row tiles when they cover the chip
 // unsplit, else 64-row tiles (32 for M <= 32) and more key splits, which keep
 // each workgroup's K/V stream short.
-int variant_for(int B, int M, int N) {
+int variant_for(int B, int M, int N, int D) {
+    if (D == 128) return kVariantDecode128;
     if (M <= 32) return kVariantDecode;
     const long long two = std::min(2LL, max_splits(N));
     if (M > 128 && (long long)B * ceil_div(M, 256) * two >= kCUs) return kVariantLarge;
@@ -66,15 +68,17 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 
 }  // namespace
 
-int make_plan(int B, int M, int N, int splits, Plan *p) {
+int make_plan(int B, int M, int N, int D, int splits, Plan *p) {
     if (B < 0 || M < 0 || N < 1 || splits < 0) return MGA_ERR_INVALID_VALUE;
+    if (D != 64 && D != 128) return MGA_ERR_CONFIG;
     if (N % 8 != 0) return MGA_ERR_LAYOUT;
     const long long nblocks = ceil_div(N, kKeyBlock);
     if (splits > nblocks) return MGA_ERR_CONFIG;
     p->B = B;
     p->M = M;
     p->N = N;
-    p->variant = variant_for(B, M, N);
+    p->D = D;
+    p->variant = variant_for(B, M, N, D);
     p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;
@@ -82,13 +86,13 @@ int make_plan(int B, int M, int N, int splits, Plan *p) {
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);
-    if (N > kMaxKeys) return MGA_ERR_CONFIG;
+    if (N > max_keys(D)) return MGA_ERR_CONFIG;
     const long long groups = ceil_div((long long)B * p->splits, 8) * 8 * p->mtiles;
-    if (groups > INT_MAX || (long long)B * M > INT_MAX / kHeadDim) return MGA_ERR_CONFIG;
+    if (groups > INT_MAX || (long long)B * M > INT_MAX / D) return MGA_ERR_CONFIG;
     if (p->splits > 1) {
-        // o_s fp16 [splits][B][M][64] rounded up to 256 bytes, then L_s fp32 [splits][B][M]
+        // o_s fp16 [splits][B][M][D] rounded up to 256 bytes, then L_s fp32 [splits][B][M]
         const size_t rows = (size_t)p->splits * B * M;
-        const size_t o_bytes = (rows * kHeadDim * 2 + 255) & ~(size_t)255;
+        const size_t o_bytes = (rows * D * 2 + 255) & ~(size_t)255;
         p->ws_bytes = (o_bytes + rows * sizeof(float) + 255) & ~(size_t)255;
     } else {
         p->ws_bytes = 0;
@@ -119,53 +123,54 @@ const char *mga_status_string(int status) {
     case MGA_ERR_LAYOUT:
         return "MGA_ERR_LAYOUT: pointer not 16-byte aligned or N not a multiple of 8";
     case MGA_ERR_CONFIG:
-        return "MGA_ERR_CONFIG: splits above ceil(N/128), N above 2^24-1, or a grid too large";
+        return "MGA_ERR_CONFIG: head dim not 64 or 128, splits above ceil(N/128), N above 2^30/D - 1, "
+               "or a grid too large";
     case MGA_ERR_WORKSPACE: return "MGA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MGA_ERR_HIP: return "MGA_ERR_HIP: kernel launch failed";
     default: return "unknown mga status";
     }
 }
 
-int mga_gqa_choose_splits(int B, int M, int N) {
+int mga_gqa_choose_splits(int B, int M, int N, int D) {
     mga::Plan p;
-    if (mga::make_plan(B, M, N, 0, &p) != MGA_OK) return 1;
+    if (mga::make_plan(B, M, N, D, 0, &p) != MGA_OK) return 1;
     return p.splits;
 }
 
-int mga_gqa_effective_splits(int B, int M, int N, int splits) {
+int mga_gqa_effective_splits(int B, int M, int N, int D, int splits) {
     mga::Plan p;
-    if (mga::make_plan(B, M, N, splits, &p) != MGA_OK) return -1;
+    if (mga::make_plan(B, M, N, D, splits, &p) != MGA_OK) return -1;
     return p.splits;
 }
 
-size_t mga_gqa_workspace_bytes(int B, int M, int N, int splits) {
+size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits) {
     mga::Plan p;
-    if (mga::make_plan(B, M, N, splits, &p) != MGA_OK) return 0;
+    if (mga::make_plan(B, M, N, D, splits, &p) != MGA_OK) return 0;
     return p.ws_bytes;
 }
 
 int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o, int B, int M,
-                       int N, int splits, const void *ws, size_t ws_bytes) {
+                       int N, int D, int splits, const void *ws, size_t ws_bytes) {
     mga::Plan p;
-    const int rc = mga::make_plan(B, M, N, splits, &p);
+    const int rc = mga::make_plan(B, M, N, D, splits, &p);
     if (rc != MGA_OK) return rc;
     return mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
 }
 
 int mga_gqa_partial(const void *q, const void *k, const void *v, void *o, int B, int M, int N,
-                    int splits, void *ws, size_t ws_bytes, void *stream) {
+                    int D, int splits, void *ws, size_t ws_bytes, void *stream) {
     mga::Plan p;
-    int rc = mga::make_plan(B, M, N, splits, &p);
+    int rc = mga::make_plan(B, M, N, D, splits, &p);
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0) return MGA_OK;
     return mga::launch_partial(p, q, k, v, o, ws, stream) == 0 ? MGA_OK : MGA_ERR_HIP;
 }
 
-int mga_gqa_combine(void *o, int B, int M, int N, int splits, const void *ws, size_t ws_bytes,
-                    void *stream) {
+int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits, const void *ws,
+                    size_t ws_bytes, void *stream) {
     mga::Plan p;
-    int rc = mga::make_plan(B, M, N, splits, &p);
+    int rc = mga::make_plan(B, M, N, D, splits, &p);
     if (rc == MGA_OK) rc = mga::check_call(nullptr, nullptr, nullptr, o, p, ws, ws_bytes, false);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0 || p.splits == 1) return MGA_OK;
@@ -173,9 +178,9 @@ int mga_gqa_combine(void *o, int B, int M, int N, int splits, const void *ws, si
 }
 
 int mga_gqa_forward(const void *q, const void *k, const void *v, void *o, int B, int M, int N,
-                    int splits, void *ws, size_t ws_bytes, void *stream) {
+                    int D, int splits, void *ws, size_t ws_bytes, void *stream) {
     mga::Plan p;
-    int rc = mga::make_plan(B, M, N, splits, &p);
+    int rc = mga::make_plan(B, M, N, D, splits, &p);
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0) return MGA_OK;
@@ -184,9 +189,9 @@ int mga_gqa_forward(const void *q, const void *k, const void *v, void *o, int B,
     return MGA_OK;
 }
 
-int mga_gqa_plan(int B, int M, int N, int splits, int *tile_rows, int *eff_splits) {
+int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits) {
     mga::Plan p;
-    const int rc = mga::make_plan(B, M, N, splits, &p);
+    const int rc = mga::make_plan(B, M, N, D, splits, &p);
     if (rc != MGA_OK) return rc;
     if (tile_rows) *tile_rows = p.tile_rows;
     if (eff_splits) *eff_splits = p.splits;

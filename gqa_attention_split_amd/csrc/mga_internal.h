@@ -7,7 +7,7 @@ namespace mga {
 
 // Geometry of one launch, decided on the host before anything is enqueued.
 struct Plan {
-    int B, M, N;
+    int B, M, N, D;
     int variant;      // kernel shape, one of the kVariant* values
     int tile_rows;    // query rows per workgroup
     int mtiles;       // ceil(M / tile_rows)
@@ -23,15 +23,18 @@ constexpr int kVariantDecode = 0;  // (1, 1, 8),  32 rows per workgroup, wave-pr
 constexpr int kVariantSmall = 1;   // (2, 1, 8),  64 rows per workgroup, wave-private rings
 constexpr int kVariantMedium = 2;  // (2, 2, 4), 128 rows per workgroup, shared ring
 constexpr int kVariantLarge = 3;   // (2, 4, 2), 256 rows per workgroup, shared ring
+// Head dim 128: (1, 1, 4), 32 rows per workgroup, 4 waves with wave-private
+// rings of two 16 KiB tiles.
+constexpr int kVariantDecode128 = 4;
 
 constexpr int kKeyBlock = 128;
-// Buffer descriptors address one batch's K or V with 32-bit byte offsets.
-constexpr int kMaxKeys = (1 << 24) - 1;
-constexpr int kHeadDim = 64;
+// Buffer descriptors address one batch's K or V with 32-bit byte offsets:
+// D * N * 2 bytes stay below 2^31.
+constexpr int max_keys(int D) { return (1 << 30) / D - 1; }
 constexpr int kThreads = 256;
 
 // Fills `p` for a call; returns an mga_status (0 = ok). Host only, no HIP calls.
-int make_plan(int B, int M, int N, int splits, Plan *p);
+int make_plan(int B, int M, int N, int D, int splits, Plan *p);
 
 // Argument checks shared by every entry point (host only).
 int check_call(const void *q, const void *k, const void *v, const void *o, const Plan &p,

@@ -49,14 +49,18 @@ class GqaConfig:
         return 2 * self.D * (2 * self.B * self.M + 2 * self.B * self.N)
 
 
-# The five workloads: the tutorial shape at batch 1 and batch 8, a long-KV
-# case, a decode-like case with few query rows, and a large-batch case.
+# The workloads: the tutorial shape at batch 1 and batch 8, a long-KV case, a
+# decode-like case with few query rows, a large-batch case, and the
+# tutorial's launch example at head dim 128 (Q (64, 1, 128), K (64, 128, 4096),
+# V (64, 4096, 128): one query row per KV head, i.e. decoding).
 CONFIGS = {
     "gqa_b2_m256_n4096": GqaConfig("gqa_b2_m256_n4096", 2, 256, 4096, 0.25, "normal", 101),
     "gqa_b16_m256_n4096": GqaConfig("gqa_b16_m256_n4096", 16, 256, 4096, 0.25, "normal", 102),
     "gqa_b2_m256_n32768": GqaConfig("gqa_b2_m256_n32768", 2, 256, 32768, 0.2, "normal", 103),
     "gqa_b64_m8_n8192": GqaConfig("gqa_b64_m8_n8192", 64, 8, 8192, 0.25, "normal", 104),
     "gqa_b128_m256_n16384": GqaConfig("gqa_b128_m256_n16384", 128, 256, 16384, 0.2, "uniform", 105),
+    "gqa_b64_m1_n4096_d128": GqaConfig("gqa_b64_m1_n4096_d128", 64, 1, 4096, 0.25, "normal", 106,
+                                       D=128),
 }
 CONFIG_ORDER = list(CONFIGS)
 BENCH_CONFIG = "gqa_b16_m256_n4096"

@@ -20,12 +20,14 @@
  *     W_s = sum_{n in split s} e_n V[n],  L_s = sum_{n in split s} e_n.
  *
  * Data layout (all row-major, contiguous, IEEE fp16, device memory):
- *     q [B][M][64]     query rows (axis 0 = batch x KV heads)
- *     k [B][64][N]     keys stored head-dim-major ("pre-transposed")
- *     v [B][N][64]     values
- *     o [B][M][64]     output, written with round-to-nearest-even
- * The head dimension is fixed at 64. Pointers must be 16-byte aligned and N a
- * multiple of 8 (every K row then starts on a 16-byte boundary).
+ *     q [B][M][D]      query rows (axis 0 = batch x KV heads)
+ *     k [B][D][N]      keys stored head-dim-major ("pre-transposed")
+ *     v [B][N][D]      values
+ *     o [B][M][D]      output, written with round-to-nearest-even
+ * The head dimension D is 64 (the tutorial graph) or 128 (the tutorial's
+ * launch example: Q (64, 1, 128), K (64, 128, 4096), V (64, 4096, 128)).
+ * Pointers must be 16-byte aligned and N a multiple of 8 (every K row then
+ * starts on a 16-byte boundary); N is at most 2^30 / D - 1.
  *
  * Numerics: fp16 MFMA products with fp32 accumulation; E = exp(A) in fp32
  * via the hardware exp2 of log2(e) Q rounded to fp16; P = fp16(E), rounded to
@@ -64,15 +66,17 @@ typedef enum {
     MGA_OK = 0,
     MGA_ERR_INVALID_VALUE = 1, /* null pointer, B or M < 0, N < 1, splits < 0      */
     MGA_ERR_LAYOUT = 2,        /* pointer not 16-byte aligned, or N % 8 != 0        */
-    MGA_ERR_CONFIG = 3,        /* splits > ceil(N / 128), N > 2^24 - 1, grid too big */
+    MGA_ERR_CONFIG = 3,        /* D not 64/128, splits > ceil(N / 128), N > 2^30/D - 1,
+                                  grid too big                                      */
     MGA_ERR_WORKSPACE = 4,     /* workspace missing, misaligned or too small        */
     MGA_ERR_HIP = 5            /* a kernel launch failed                            */
 } mga_status;
 
 /* Keys per pipeline stage; split chunks are whole multiples of it. */
 #define MGA_KEY_BLOCK 128
-/* Head dimension supported by this build. */
+/* Head dimensions supported by this build. */
 #define MGA_HEAD_DIM 64
+#define MGA_HEAD_DIM_WIDE 128
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *mga_status_string(int status);
@@ -82,35 +86,35 @@ const char *mga_status_string(int status);
  * [1, ceil(N / 128)]; returns 1 for N < 1. Following the kaispace blog
  * (section 4.2), the split count is a grid-dimension choice; here a fixed
  * rule picks it instead of a search. */
-int mga_gqa_choose_splits(int B, int M, int N);
+int mga_gqa_choose_splits(int B, int M, int N, int D);
 
 /* The split count actually launched for a requested `splits` (0 = policy):
  * the chunk is ceil(ceil(N/128) / splits) key blocks and the count is
  * ceil(ceil(N/128) / chunk), so that no split is empty. Returns -1 for
  * arguments mga_gqa_check_args would reject with INVALID_VALUE or CONFIG. */
-int mga_gqa_effective_splits(int B, int M, int N, int splits);
+int mga_gqa_effective_splits(int B, int M, int N, int D, int splits);
 
 /* Bytes of workspace mga_gqa_forward needs: 0 when the effective split count
- * s is 1; else the normalised partials o[s][B][M][64] in fp16 (s*B*M*128
+ * s is 1; else the normalised partials o[s][B][M][D] in fp16 (s*B*M*D*2
  * bytes, rounded up to 256) followed by the denominators L[s][B][M] in fp32
  * (s*B*M*4 bytes), the total rounded up to 256. Its contents need no
  * initialisation. Returns 0 for invalid shapes. */
-size_t mga_gqa_workspace_bytes(int B, int M, int N, int splits);
+size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
 
 /* The launch geometry the library picks (host only): query rows per
- * workgroup (32, 64, 128 or 256: the largest tile whose workgroups still
- * cover all 256 compute units without splitting, else 64, or 32 for M <= 32)
- * and the effective split count. Either output pointer may be NULL. Returns
- * the status mga_gqa_check_args would give for the shape (MGA_OK,
- * INVALID_VALUE, LAYOUT or CONFIG). */
-int mga_gqa_plan(int B, int M, int N, int splits, int *tile_rows, int *eff_splits);
+ * workgroup (D = 64: 32, 64, 128 or 256 -- the largest tile whose workgroups
+ * still cover all 256 compute units without splitting, else 64, or 32 for
+ * M <= 32; D = 128: 32) and the effective split count. Either output pointer
+ * may be NULL. Returns the status mga_gqa_check_args would give for the shape
+ * (MGA_OK, INVALID_VALUE, LAYOUT or CONFIG). */
+int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
 
 /* Host-only validation of a forward call; makes no HIP call and launches
  * nothing, so it is usable without a GPU. Returns the status
  * mga_gqa_forward would return before launching. `ws` may be NULL when the
  * effective split count is 1. B == 0 or M == 0 is valid (a no-op). */
 int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o,
-                       int B, int M, int N, int splits, const void *ws, size_t ws_bytes);
+                       int B, int M, int N, int D, int splits, const void *ws, size_t ws_bytes);
 
 /* The whole path: partial kernel, then (when the effective split count is
  * above 1) the combine kernel, both on `stream`. splits = 0 lets the policy
@@ -118,7 +122,7 @@ int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *
  * mga_gqa_workspace_bytes(B, M, N, splits) bytes, 16-byte aligned. Calls
  * that share a workspace must not overlap in time. */
 int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
-                    int B, int M, int N, int splits, void *ws, size_t ws_bytes,
+                    int B, int M, int N, int D, int splits, void *ws, size_t ws_bytes,
                     void *stream);
 
 /* Only the split-KV partial kernel (the for-loop over keys). With one
@@ -126,7 +130,7 @@ int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
  * writes the normalised partials and denominators into `ws` and leaves `o`
  * untouched. Same arguments and checks as mga_gqa_forward. */
 int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
-                    int B, int M, int N, int splits, void *ws, size_t ws_bytes,
+                    int B, int M, int N, int D, int splits, void *ws, size_t ws_bytes,
                     void *stream);
 
 /* Only the combine kernel:
@@ -134,7 +138,7 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
  * with the sums taken in split order (fp32). `ws` holds the partials a preceding
  * mga_gqa_partial call wrote for the same (B, M, N, splits); q, k and v are
  * not read. A no-op returning MGA_OK when the effective split count is 1. */
-int mga_gqa_combine(void *o, int B, int M, int N, int splits,
+int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits,
                     const void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus

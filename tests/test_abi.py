@@ -45,10 +45,10 @@ def test_status_strings():
     assert "unknown" in mga.mga_status_string(99)
 
 
-def _check(B=2, M=256, N=4096, splits=0, q=A, k=A, v=A, o=A, ws=A, ws_bytes=None):
+def _check(B=2, M=256, N=4096, splits=0, q=A, k=A, v=A, o=A, ws=A, ws_bytes=None, D=64):
     if ws_bytes is None:
-        ws_bytes = mga.mga_gqa_workspace_bytes(B, M, N, splits)
-    return mga.mga_gqa_check_args(q, k, v, o, B, M, N, splits, ws, ws_bytes)
+        ws_bytes = mga.mga_gqa_workspace_bytes(B, M, N, D, splits)
+    return mga.mga_gqa_check_args(q, k, v, o, B, M, N, D, splits, ws, ws_bytes)
 
 
 def test_check_args_codes():
@@ -74,52 +74,79 @@ def test_check_args_codes():
     assert _check(M=0, q=None, k=None, v=None, o=None, ws=None, ws_bytes=0) == mga.MGA_OK
 
 
+def test_check_args_head_dim():
+    assert _check(D=128) == mga.MGA_OK
+    assert _check(D=128, splits=4) == mga.MGA_OK
+    assert _check(D=128, splits=4, ws_bytes=mga.mga_gqa_workspace_bytes(2, 256, 4096, 64, 4)) == \
+        mga.MGA_ERR_WORKSPACE                                 # sized for D = 64: too small
+    for D in (0, -64, 32, 96, 256):
+        assert _check(D=D) == mga.MGA_ERR_CONFIG, D
+    # N * D * 2 bytes must stay below 2^31: N <= 2^23 - 1 at D = 128, 2^24 - 1 at D = 64
+    assert _check(D=128, N=(1 << 23) - 8, splits=1) == mga.MGA_OK
+    assert _check(D=128, N=1 << 23, splits=1) == mga.MGA_ERR_CONFIG
+    assert _check(D=64, N=1 << 23, splits=1) == mga.MGA_OK
+    assert _check(D=64, N=(1 << 24) - 8, splits=1) == mga.MGA_OK
+    # B * M * D must stay below 2^31 elements
+    assert _check(D=128, B=65535, M=256, N=8) == mga.MGA_OK
+    assert _check(D=128, B=65536, M=256, N=8) == mga.MGA_ERR_CONFIG
+    assert _check(D=64, B=65536, M=256, N=8) == mga.MGA_OK
+    assert _check(D=64, B=65536, M=512, N=8) == mga.MGA_ERR_CONFIG
+
+
 def test_forward_rejects_before_launching():
     # Errors come back before any HIP call, so this runs without a GPU.
-    assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4100, 0, None, 0, None) == mga.MGA_ERR_LAYOUT
-    assert mga.mga_gqa_partial(None, A, A, A, 2, 256, 4096, 1, None, 0, None) == \
+    assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4100, 64, 0, None, 0, None) == mga.MGA_ERR_LAYOUT
+    assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4096, 80, 1, None, 0, None) == mga.MGA_ERR_CONFIG
+    assert mga.mga_gqa_partial(None, A, A, A, 2, 256, 4096, 128, 1, None, 0, None) == \
         mga.MGA_ERR_INVALID_VALUE
-    assert mga.mga_gqa_combine(A, 2, 256, 4096, 4, None, 0, None) == mga.MGA_ERR_WORKSPACE
-    assert mga.mga_gqa_forward(None, None, None, None, 0, 256, 4096, 0, None, 0, None) == mga.MGA_OK
+    assert mga.mga_gqa_combine(A, 2, 256, 4096, 64, 4, None, 0, None) == mga.MGA_ERR_WORKSPACE
+    assert mga.mga_gqa_combine(A, 2, 256, 4096, 128, 4, A, 1024, None) == mga.MGA_ERR_WORKSPACE
+    assert mga.mga_gqa_forward(None, None, None, None, 0, 256, 4096, 64, 0, None, 0, None) == \
+        mga.MGA_OK
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,M,N", [(2, 256, 4096), (16, 256, 4096), (2, 256, 32768),
                                    (64, 8, 8192), (128, 256, 16384), (1, 1, 8), (3, 17, 136),
-                                   (5, 100, 1000), (1, 300, 129 * 8)])
-def test_split_policy_and_workspace(B, M, N):
+                                   (5, 100, 1000), (1, 300, 129 * 8), (64, 1, 4096)])
+def test_split_policy_and_workspace(B, M, N, D):
     nblocks = math.ceil(N / mga.KEY_BLOCK)
-    s = mga.mga_gqa_choose_splits(B, M, N)
+    s = mga.mga_gqa_choose_splits(B, M, N, D)
     assert 1 <= s <= nblocks
     for req in sorted({r for r in (0, 1, 2, 3, 7, nblocks) if r <= nblocks}):
-        eff = mga.mga_gqa_effective_splits(B, M, N, req)
+        eff = mga.mga_gqa_effective_splits(B, M, N, D, req)
         want = s if req == 0 else req
         chunk = math.ceil(nblocks / want)
         assert eff == math.ceil(nblocks / chunk)
         assert 1 <= eff <= want
         assert (eff - 1) * chunk < nblocks          # no empty split
-        ws = mga.mga_gqa_workspace_bytes(B, M, N, req)
-        rc, rows, eff2 = mga.mga_gqa_plan(B, M, N, req)
-        assert rc == mga.MGA_OK and eff2 == eff and rows in (32, 64, 128, 256)
+        ws = mga.mga_gqa_workspace_bytes(B, M, N, D, req)
+        rc, rows, eff2 = mga.mga_gqa_plan(B, M, N, D, req)
+        assert rc == mga.MGA_OK and eff2 == eff and rows in ((32, 64, 128, 256) if D == 64 else (32,))
         if eff == 1:
             assert ws == 0
         else:
-            o_bytes = -(-eff * B * M * 128 // 256) * 256     # fp16 partials, then fp32 denominators
+            o_bytes = -(-eff * B * M * D * 2 // 256) * 256   # fp16 partials, then fp32 denominators
             assert ws == -(-(o_bytes + eff * B * M * 4) // 256) * 256
-    assert mga.mga_gqa_effective_splits(B, M, N, nblocks + 1) == -1
-    assert mga.mga_gqa_plan(B, M, N, nblocks + 1)[0] == mga.MGA_ERR_CONFIG
+    assert mga.mga_gqa_effective_splits(B, M, N, D, nblocks + 1) == -1
+    assert mga.mga_gqa_plan(B, M, N, D, nblocks + 1)[0] == mga.MGA_ERR_CONFIG
 
 
-@pytest.mark.parametrize("B,M,N,rows,splits", [
-    (16, 256, 4096, 64, 4),      # few query rows: 64-row tiles, 4 splits fill 256 CUs
-    (2, 256, 4096, 64, 8),       # 32 would fill the chip; chunks keep >= 4 key blocks
-    (2, 256, 32768, 64, 32),
-    (64, 8, 8192, 32, 4),        # decode-like rows: 32-row tiles
-    (128, 256, 16384, 256, 2),   # 256-row tiles fill the chip with two splits
-    (128, 130, 520, 128, 1),     # 128-row tiles fill the chip unsplit
-    (1024, 256, 1024, 256, 1),   # 256-row tiles already fill the chip
+@pytest.mark.parametrize("B,M,N,D,rows,splits", [
+    (64, 1, 4096, 128, 32, 4),   # the head-dim-128 decode example: 4 splits fill 256 CUs
+    (8, 32, 16384, 128, 32, 32),
+    (1, 1, 8, 128, 32, 1),
+    (256, 64, 1024, 128, 32, 1),
+    (16, 256, 4096, 64, 64, 4),      # few query rows: 64-row tiles, 4 splits fill 256 CUs
+    (2, 256, 4096, 64, 64, 8),       # 32 would fill the chip; chunks keep >= 4 key blocks
+    (2, 256, 32768, 64, 64, 32),
+    (64, 8, 8192, 64, 32, 4),        # decode-like rows: 32-row tiles
+    (128, 256, 16384, 64, 256, 2),   # 256-row tiles fill the chip with two splits
+    (128, 130, 520, 64, 128, 1),     # 128-row tiles fill the chip unsplit
+    (1024, 256, 1024, 64, 256, 1),   # 256-row tiles already fill the chip
 ])
-def test_plan_policy(B, M, N, rows, splits):
-    assert mga.mga_gqa_plan(B, M, N, 0) == (mga.MGA_OK, rows, splits)
+def test_plan_policy(B, M, N, D, rows, splits):
+    assert mga.mga_gqa_plan(B, M, N, D, 0) == (mga.MGA_OK, rows, splits)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -85,14 +85,14 @@ def sample_rows(M, n, seed):
 
 # Full-size workloads, in the launch configuration the bench times (policy splits).
 ROWS_PER_BATCH = {"gqa_b2_m256_n4096": 256, "gqa_b16_m256_n4096": 24, "gqa_b2_m256_n32768": 48,
-                  "gqa_b64_m8_n8192": 8, "gqa_b128_m256_n16384": 6}
+                  "gqa_b64_m8_n8192": 8, "gqa_b128_m256_n16384": 6, "gqa_b64_m1_n4096_d128": 1}
 
 
 @pytest.mark.parametrize("name", CONFIG_ORDER)
 def test_full_size_workload_sampled_rows(gpu, name):
     cfg = CONFIGS[name]
-    _say(f"[parity] {name} B={cfg.B} M={cfg.M} N={cfg.N} seed={cfg.seed} "
-         f"splits={mga.mga_gqa_choose_splits(cfg.B, cfg.M, cfg.N)}")
+    _say(f"[parity] {name} B={cfg.B} M={cfg.M} N={cfg.N} D={cfg.D} seed={cfg.seed} "
+         f"splits={mga.mga_gqa_choose_splits(cfg.B, cfg.M, cfg.N, cfg.D)}")
     q, k, v = make_config(cfg)
     o = run_gpu(q, k, v, gpu)
     rows = sample_rows(cfg.M, ROWS_PER_BATCH[name], cfg.seed)
@@ -105,15 +105,17 @@ SMALL = [(1, 1, 8), (1, 16, 8), (1, 8, 72), (2, 17, 136), (1, 64, 128), (2, 129,
          (3, 255, 4104), (2, 300, 1000), (4, 65, 520), (1, 256, 2048)]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,M,N", SMALL)
-def test_small_and_ragged_shapes_all_splits(gpu, B, M, N):
-    q, k, v = make_qkv(B, M, N, seed=1000 + B * 7 + M * 3 + N, qk_std=0.3)
+def test_small_and_ragged_shapes_all_splits(gpu, B, M, N, D):
+    q, k, v = make_qkv(B, M, N, seed=1000 + B * 7 + M * 3 + N + D, qk_std=0.3 if D == 64 else 0.25,
+                       D=D)
     ref = oracle.gqa_f64(q, k, v)
     nblocks = -(-N // mga.KEY_BLOCK)
     for s in sorted({0, 1, 2, 3, 7, nblocks} & set(range(0, nblocks + 1))):
-        _say(f"[parity] B={B} M={M} N={N} splits={s} "
-             f"(effective {mga.mga_gqa_effective_splits(B, M, N, s)})")
-        assert_parity(run_gpu(q, k, v, gpu, splits=s), ref, q, k, v, f"B{B} M{M} N{N} s{s}")
+        _say(f"[parity] B={B} M={M} N={N} D={D} splits={s} "
+             f"(effective {mga.mga_gqa_effective_splits(B, M, N, D, s)})")
+        assert_parity(run_gpu(q, k, v, gpu, splits=s), ref, q, k, v, f"B{B} M{M} N{N} D{D} s{s}")
 
 
 def _quantized(shape, seed, scale):
@@ -122,59 +124,66 @@ def _quantized(shape, seed, scale):
     return (rng.integers(-128, 128, size=shape, dtype=np.int8).astype(np.float16) * np.float16(scale))
 
 
-def test_largest_key_count(gpu):
-    """N at the top of the supported range (2^24 - 8): a batch's K and V byte
-    offsets reach 2^31, the per-lane K offsets d*N*2 their maximum, and the
-    last tile straddles N. Policy splits and one split per 128-key block."""
+@pytest.mark.parametrize("D", [64, 128])
+def test_largest_key_count(gpu, D):
+    """N at the top of the supported range (2^30 / D - 8: 2^24 - 8 at D = 64,
+    2^23 - 8 at D = 128): a batch's K and V byte offsets reach 2^31, the
+    per-lane K offsets d*N*2 their maximum, and the last tile straddles N.
+    Policy splits and one split per 128-key block."""
     import torch
-    B, M, N = 1, 2, (1 << 24) - 8
-    q = _quantized((B, M, 64), 901, 1 / 256)            # |q| <= 0.5
-    k = _quantized((B, 64, N), 902, 1 / 512)            # |k| <= 0.25: |score| <= 64 * 0.5 * 0.25 = 8 < ln 65504
-    v = _quantized((B, N, 64), 903, 1 / 64)             # |v| <= 2
+    B, M, N = 1, 2, (1 << 30) // D - 8
+    q = _quantized((B, M, D), 901, 1 / 256)             # |q| <= 0.5
+    # |k| <= 16 / D: |score| <= D * 0.5 * 16 / D = 8 < ln 65504
+    k = _quantized((B, D, N), 902, 1 / (8 * D))
+    v = _quantized((B, N, D), 903, 1 / 64)              # |v| <= 2
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
     ref = oracle.gqa_f64(q, k, v)
     nblocks = -(-N // mga.KEY_BLOCK)
     for s in (0, nblocks):
-        _say(f"[max N] B={B} M={M} N={N} splits={s} (effective {mga.mga_gqa_effective_splits(B, M, N, s)}, "
-             f"workspace {mga.mga_gqa_workspace_bytes(B, M, N, s)} B)")
+        _say(f"[max N] B={B} M={M} N={N} D={D} splits={s} "
+             f"(effective {mga.mga_gqa_effective_splits(B, M, N, D, s)}, "
+             f"workspace {mga.mga_gqa_workspace_bytes(B, M, N, D, s)} B)")
         o = mga.gqa_forward(tq, tk, tv, splits=s)
         torch.cuda.synchronize()
-        assert_parity(o.cpu().numpy(), ref, q, k, v, f"max N s{s}")
+        assert_parity(o.cpu().numpy(), ref, q, k, v, f"max N D{D} s{s}")
     del tq, tk, tv
     torch.cuda.empty_cache()
 
 
-def test_many_query_rows(gpu):
-    """65536 batch rows x 256 queries (4 GiB of Q and of O) over 8 keys: row
-    and batch offsets past 2^31 elements' worth of bytes, a 65536-workgroup
-    grid; checked on sampled rows of every 4096th batch."""
+@pytest.mark.parametrize("B,D", [(65536, 64), (65535, 128)])
+def test_many_query_rows(gpu, B, D):
+    """B batch rows x 256 queries over 8 keys, B * 256 * D just below 2^31
+    elements (4 GiB of Q and of O): row and batch byte offsets past 2^31, a
+    grid of 65536 (D = 64) or 524280 (D = 128) workgroups; checked on sampled
+    rows of every 4096th batch."""
     import torch
-    B, M, N = 65536, 256, 8
-    q = _quantized((B, M, 64), 911, 1 / 256)
-    k = _quantized((B, 64, N), 912, 1 / 256)
-    v = _quantized((B, N, 64), 913, 1 / 64)
+    M, N = 256, 8
+    q = _quantized((B, M, D), 911, 1 / 256)
+    k = _quantized((B, D, N), 912, 1 / (4 * D))        # |k| <= 32 / D, as at D = 64 before
+    v = _quantized((B, N, D), 913, 1 / 64)
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
-    _say(f"[many rows] B={B} M={M} N={N} plan={mga.mga_gqa_plan(B, M, N, 0)}")
+    _say(f"[many rows] B={B} M={M} N={N} D={D} plan={mga.mga_gqa_plan(B, M, N, D, 0)}")
     o = mga.gqa_forward(tq, tk, tv).cpu().numpy()
     torch.cuda.synchronize()
     bs = np.arange(0, B, 4096).tolist() + [B - 1]
     rows = sample_rows(M, 8, 5)
     qs = np.ascontiguousarray(q[bs][:, rows])
     ks, vs = np.ascontiguousarray(k[bs]), np.ascontiguousarray(v[bs])
-    assert_parity(o[bs][:, rows], oracle.gqa_f64(qs, ks, vs), qs, ks, vs, "many rows")
+    assert_parity(o[bs][:, rows], oracle.gqa_f64(qs, ks, vs), qs, ks, vs, f"many rows D{D}")
     del tq, tk, tv
     torch.cuda.empty_cache()
 
 
-def test_split_invariance_and_determinism(gpu):
-    cfg = CONFIGS["gqa_b16_m256_n4096"]
+@pytest.mark.parametrize("name", ["gqa_b16_m256_n4096", "gqa_b64_m1_n4096_d128"])
+def test_split_invariance_and_determinism(gpu, name):
+    cfg = CONFIGS[name]
     q, k, v = make_config(cfg)
     rows = sample_rows(cfg.M, 16, 7)
     qr = np.ascontiguousarray(q[:, rows])
     ref = oracle.gqa_f64(qr, k, v)
     outs = {}
     for s in (1, 2, 3, 7, 16, 32):
-        _say(f"[split-invariance] splits={s}")
+        _say(f"[split-invariance] {name} splits={s}")
         o1 = run_gpu(q, k, v, gpu, splits=s)
         o2 = run_gpu(q, k, v, gpu, splits=s)
         assert o1.tobytes() == o2.tobytes(), f"splits={s}: run-to-run bits differ"
@@ -185,9 +194,10 @@ def test_split_invariance_and_determinism(gpu):
         assert np.max(np.abs(o.astype(np.float64) - base)) <= 2e-4
 
 
-def test_structured_inputs_expose_dropped_or_duplicated_keys(gpu):
-    B, M, N = 3, 200, 64 * 37  # 2368 keys: ragged last block
-    q, k, v = make_qkv(B, M, N, seed=77, qk_std=0.3)
+@pytest.mark.parametrize("D", [64, 128])
+def test_structured_inputs_expose_dropped_or_duplicated_keys(gpu, D):
+    B, M, N = 3, 200, D * 37  # 2368 or 4736 keys: ragged last block
+    q, k, v = make_qkv(B, M, N, seed=77, qk_std=0.3 if D == 64 else 0.25, D=D)
     v = v.copy()
     v[:, :, 7] = 1.0            # ones column: weights sum to 1 exactly in the kernel's sums
     for s in (1, 3, 0):
@@ -200,68 +210,72 @@ def test_structured_inputs_expose_dropped_or_duplicated_keys(gpu):
     mean = np.broadcast_to(v.astype(np.float64).mean(axis=1, keepdims=True), o.shape)
     assert_parity(o, np.ascontiguousarray(mean), q0, k, v, "Q=0 mean")
     # Chunk-indicator V: column j is the weight mass of key range j.
-    r = N // 64
-    vi = np.zeros((B, N, 64), np.float16)
+    r = N // D
+    vi = np.zeros((B, N, D), np.float16)
     for n in range(N):
         vi[:, n, n // r] = 1.0
     for s in (1, 5, 0):
         o = run_gpu(q, k, vi, gpu, splits=s)
         assert_parity(o, oracle.gqa_f64(q, k, vi), q, k, vi, f"chunk-indicator s{s}")
-        assert np.max(np.abs(o.astype(np.float64).sum(axis=2) - 1.0)) <= 64 * 2e-4
+        assert np.max(np.abs(o.astype(np.float64).sum(axis=2) - 1.0)) <= D * 2e-4
 
 
-def test_partial_then_combine_matches_forward(gpu):
+@pytest.mark.parametrize("D", [64, 128])
+def test_partial_then_combine_matches_forward(gpu, D):
     import torch
     B, M, N = 4, 256, 4096
-    q, k, v = make_qkv(B, M, N, seed=5, qk_std=0.25)
+    q, k, v = make_qkv(B, M, N, seed=5, qk_std=0.25, D=D)
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
     for s in (1, 4):
         o_fwd = mga.gqa_forward(tq, tk, tv, splits=s)
         o = torch.empty_like(o_fwd)
-        ws = mga.workspace_for(B, M, N, s, device=gpu)
+        ws = mga.workspace_for(B, M, N, D, s, device=gpu)
         nb = 0 if ws is None else ws.numel()
         stream = torch.cuda.current_stream()
-        assert mga.mga_gqa_partial(tq, tk, tv, o, B, M, N, s, ws, nb, stream) == mga.MGA_OK
-        assert mga.mga_gqa_combine(o, B, M, N, s, ws, nb, stream) == mga.MGA_OK
+        assert mga.mga_gqa_partial(tq, tk, tv, o, B, M, N, D, s, ws, nb, stream) == mga.MGA_OK
+        assert mga.mga_gqa_combine(o, B, M, N, D, s, ws, nb, stream) == mga.MGA_OK
         torch.cuda.synchronize()
         assert torch.equal(o, o_fwd)
 
 
-@pytest.mark.parametrize("B,M,N", [(16, 256, 4096), (64, 8, 8192), (3, 100, 1000),
-                                   (128, 130, 520), (128, 130, 264),     # 128-row tiles: refilled / resident ring
-                                   (256, 257, 520), (256, 260, 136)])    # 256-row tiles: refilled / resident ring
-def test_partial_then_combine_each_tile_shape(gpu, B, M, N):
-    """Every query-tile shape the plan can pick (32, 64, 128 and 256 rows,
-    wave-private and shared rings, the shared ring both refilled and with the
-    whole chunk resident): partial + combine equals forward bit for bit, and a
-    reused workspace gives the same bits on every call."""
+@pytest.mark.parametrize("B,M,N,D", [(16, 256, 4096, 64), (64, 8, 8192, 64), (3, 100, 1000, 64),
+                                     (128, 130, 520, 64), (128, 130, 264, 64),   # 128-row tiles: refilled / resident ring
+                                     (256, 257, 520, 64), (256, 260, 136, 64),   # 256-row tiles: refilled / resident ring
+                                     (64, 1, 4096, 128), (3, 33, 1000, 128)])    # head dim 128: 32-row tiles
+def test_partial_then_combine_each_tile_shape(gpu, B, M, N, D):
+    """Every query-tile shape the plan can pick (32, 64, 128 and 256 rows at
+    head dim 64, wave-private and shared rings, the shared ring both refilled
+    and with the whole chunk resident; 32 rows at head dim 128): partial +
+    combine equals forward bit for bit, and a reused workspace gives the same
+    bits on every call."""
     import torch
-    q, k, v = make_qkv(B, M, N, seed=31, qk_std=0.3)
+    q, k, v = make_qkv(B, M, N, seed=31, qk_std=0.3 if D == 64 else 0.25, D=D)
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
     nblocks = -(-N // mga.KEY_BLOCK)
     stream = torch.cuda.current_stream()
     for req in sorted({0, 2, 3, nblocks}):
         if req > nblocks:
             continue
-        rc, rows, s = mga.mga_gqa_plan(B, M, N, req)
+        rc, rows, s = mga.mga_gqa_plan(B, M, N, D, req)
         assert rc == mga.MGA_OK
-        ws = mga.workspace_for(B, M, N, req, device=gpu)
+        ws = mga.workspace_for(B, M, N, D, req, device=gpu)
         nb = 0 if ws is None else ws.numel()
-        ref = torch.empty((B, M, 64), dtype=torch.float16, device=gpu)
-        assert mga.mga_gqa_partial(tq, tk, tv, ref, B, M, N, req, ws, nb, stream) == mga.MGA_OK
-        assert mga.mga_gqa_combine(ref, B, M, N, req, ws, nb, stream) == mga.MGA_OK
+        ref = torch.empty((B, M, D), dtype=torch.float16, device=gpu)
+        assert mga.mga_gqa_partial(tq, tk, tv, ref, B, M, N, D, req, ws, nb, stream) == mga.MGA_OK
+        assert mga.mga_gqa_combine(ref, B, M, N, D, req, ws, nb, stream) == mga.MGA_OK
         for call in range(3):
-            o = torch.full((B, M, 64), float("nan"), dtype=torch.float16, device=gpu)
-            assert mga.mga_gqa_forward(tq, tk, tv, o, B, M, N, req, ws, nb, stream) == mga.MGA_OK
+            o = torch.full((B, M, D), float("nan"), dtype=torch.float16, device=gpu)
+            assert mga.mga_gqa_forward(tq, tk, tv, o, B, M, N, D, req, ws, nb, stream) == mga.MGA_OK
             torch.cuda.synchronize()
-            _say(f"[tile shapes] B={B} M={M} N={N} splits={s} rows={rows} call {call}")
+            _say(f"[tile shapes] B={B} M={M} N={N} D={D} splits={s} rows={rows} call {call}")
             assert torch.equal(o, ref), f"forward differs from partial+combine (call {call})"
-        assert_parity(ref.cpu().numpy(), oracle.gqa_f64(q, k, v), q, k, v, f"rows{rows} s{s}")
+        assert_parity(ref.cpu().numpy(), oracle.gqa_f64(q, k, v), q, k, v, f"D{D} rows{rows} s{s}")
 
 
-def test_non_default_stream_and_empty_shapes(gpu):
+@pytest.mark.parametrize("D", [64, 128])
+def test_non_default_stream_and_empty_shapes(gpu, D):
     import torch
-    q, k, v = make_qkv(2, 40, 520, seed=9)
+    q, k, v = make_qkv(2, 40, 520, seed=9, D=D)
     ref = oracle.gqa_f64(q, k, v)
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
     s = torch.cuda.Stream()
@@ -269,8 +283,8 @@ def test_non_default_stream_and_empty_shapes(gpu):
         out = mga.gqa_forward(tq, tk, tv)
     s.synchronize()
     assert_parity(out.cpu().numpy(), ref, q, k, v, "side stream")
-    empty = torch.empty((2, 0, 64), dtype=torch.float16, device=gpu)
-    assert mga.gqa_forward(empty, tk, tv).shape == (2, 0, 64)
+    empty = torch.empty((2, 0, D), dtype=torch.float16, device=gpu)
+    assert mga.gqa_forward(empty, tk, tv).shape == (2, 0, D)
     torch.cuda.synchronize()
 
 
@@ -280,6 +294,6 @@ def test_gpu_rejects_misaligned_pointer_without_launching(gpu):
     k = torch.zeros((1, 64, 8), dtype=torch.float16, device=gpu)
     v = torch.zeros((1, 8, 64), dtype=torch.float16, device=gpu)
     o = torch.zeros((1, 8, 64), dtype=torch.float16, device=gpu)
-    rc = mga.mga_gqa_forward(buf.data_ptr() + 2, k, v, o, 1, 8, 8, 0, None, 0,
+    rc = mga.mga_gqa_forward(buf.data_ptr() + 2, k, v, o, 1, 8, 8, 64, 0, None, 0,
                              torch.cuda.current_stream())
     assert rc == mga.MGA_ERR_LAYOUT

@@ -22,8 +22,8 @@ def test_same_seed_same_bytes_and_new_seed_new_bytes():
 def test_config_shapes_dtypes_and_distributions(name):
     cfg = CONFIGS[name]
     q, k, v = make_config(cfg)
-    assert q.shape == (cfg.B, cfg.M, 64) and k.shape == (cfg.B, 64, cfg.N)
-    assert v.shape == (cfg.B, cfg.N, 64)
+    assert q.shape == (cfg.B, cfg.M, cfg.D) and k.shape == (cfg.B, cfg.D, cfg.N)
+    assert v.shape == (cfg.B, cfg.N, cfg.D)
     for x in (q, k, v):
         assert x.dtype == np.float16 and x.flags["C_CONTIGUOUS"]
     assert abs(float(q.astype(np.float64).std()) - cfg.qk_std) < 0.02 * cfg.qk_std + 1e-3
