@@ -8,9 +8,11 @@ example, Q (64, 1, 128)).
 
 The functions named ``mga_*`` mirror the C ABI in ``include/mga_gqa.h`` one to
 one and only marshal arguments (pointers may be ints or torch tensors; the
-stream may be an int handle or a torch stream). ``gqa_forward`` is the
-convenience form for torch tensors: it validates, allocates the output and
-the workspace with torch, and calls ``mga_gqa_forward``. Every step of the
+stream may be an int handle or a torch stream; strides a sequence of nine
+ints). ``gqa_forward`` is the convenience form for torch tensors: it
+validates, allocates the output and the workspace with torch, and calls
+``mga_gqa_forward`` (contiguous tensors) or ``mga_gqa_forward_strided``
+(views, e.g. K as the transpose of a (B, N, D) tensor). Every step of the
 computation runs in the HIP kernels; nothing here computes.
 """
 from __future__ import annotations
@@ -84,6 +86,27 @@ def mga_gqa_forward(q, k, v, o, B, M, N, D, splits, ws, ws_bytes, stream) -> int
                                        _ptr(ws), ws_bytes, _stream(stream))
 
 
+def _strides(st):
+    import ctypes
+    if st is None:
+        return None
+    vals = [int(x) for x in st]
+    if len(vals) != 9:
+        raise ValueError("strides: nine element strides (q_b, q_i, k_b, k_d, k_n, v_b, v_n, o_b, o_i)")
+    return ctypes.cast((ctypes.c_int64 * 9)(*vals), ctypes.c_void_p)
+
+
+def mga_gqa_forward_strided(q, k, v, o, B, M, N, D, strides, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D,
+                                               _strides(strides), splits, _ptr(ws), ws_bytes,
+                                               _stream(stream))
+
+
+def mga_gqa_check_args_strided(q, k, v, o, B, M, N, D, strides, splits, ws, ws_bytes) -> int:
+    return _lib.load().mga_gqa_check_args_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D,
+                                                  _strides(strides), splits, _ptr(ws), ws_bytes)
+
+
 def mga_gqa_partial(q, k, v, o, B, M, N, D, splits, ws, ws_bytes, stream) -> int:
     return _lib.load().mga_gqa_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D, splits,
                                        _ptr(ws), ws_bytes, _stream(stream))
@@ -102,8 +125,6 @@ def _check_tensors(q, k, v):
             raise TypeError(f"{name} must be float16, got {t.dtype}")
         if not t.is_cuda:
             raise ValueError(f"{name} must be on a GPU device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
         if t.dim() != 3:
             raise ValueError(f"{name} must be 3-D")
     B, M, D = q.shape
@@ -129,20 +150,31 @@ def workspace_for(B: int, M: int, N: int, D: int, splits: int = 0, device=None):
 
 
 def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None):
-    """O = (exp(QK) / rowsum) V for fp16 GPU tensors q (B,M,D), k (B,D,N), v (B,N,D)."""
+    """O = (exp(QK) / rowsum) V for fp16 GPU tensors q (B,M,D), k (B,D,N), v (B,N,D).
+
+    The tensors may be strided views (the library checks which layouts it
+    takes: unit stride along D for q, v and out; k with unit stride along N
+    or along D; other strides multiples of 8). ``out`` may be a view too."""
     import torch
     B, M, N, D = _check_tensors(q, k, v)
     if out is None:
         out = torch.empty((B, M, D), dtype=torch.float16, device=q.device)
-    elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, D) or \
-            not out.is_contiguous() or out.device != q.device:
-        raise ValueError(f"out must be a contiguous float16 (B, M, {D}) tensor on q's device")
+    elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, D) or out.device != q.device:
+        raise ValueError(f"out must be a float16 (B, M, {D}) tensor on q's device")
     if workspace is None:
         workspace = workspace_for(B, M, N, D, splits, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = mga_gqa_forward(q, k, v, out, B, M, N, D, splits, workspace, ws_bytes, stream)
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        rc = mga_gqa_forward(q, k, v, out, B, M, N, D, splits, workspace, ws_bytes, stream)
+    else:
+        for name, t in (("q", q), ("v", v), ("out", out)):
+            if t.stride(2) != 1 and t.shape[2] > 1:
+                raise ValueError(f"{name} needs unit stride along the head dim")
+        st = (q.stride(0), q.stride(1), k.stride(0), k.stride(1), k.stride(2), v.stride(0),
+              v.stride(1), out.stride(0), out.stride(1))
+        rc = mga_gqa_forward_strided(q, k, v, out, B, M, N, D, st, splits, workspace, ws_bytes, stream)
     if rc != MGA_OK:
         raise GqaError(rc)
     return out

@@ -25,6 +25,8 @@ SIGNATURES = {
     "mga_gqa_forward": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
     "mga_gqa_partial": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
     "mga_gqa_combine": ([_P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
+    "mga_gqa_forward_strided": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _S, _P], _I),
+    "mga_gqa_check_args_strided": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _S], _I),
 }
 
 _lib = None

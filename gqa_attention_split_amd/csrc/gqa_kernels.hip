@@ -46,16 +46,25 @@
 // normalised partial o_s = fp16(W / L) and L go to the caller's workspace for
 // the combine kernel, which forms O = sum_s L_s o_s / sum_s L_s.
 //
+// Layouts. Every operand is addressed through element strides (Strides):
+// Q, V and O rows have unit stride along the head dim; K is either
+// head-dim-major (K[d][n], unit stride along keys: the tutorial's
+// pre-transposed K) or key-major (K[n][d], e.g. the transposed view of a
+// [keys][head dim] cache). Row and batch strides are multiples of 8 elements,
+// so every 16-byte DMA unit is aligned; N itself is unrestricted.
+//
 // Bounds. K/V/Q accesses go through buffer descriptors whose record count
-// ends at the last valid byte of batch b's array (or at zero for tiles past
-// the chunk end), so out-of-range lanes read zeros. K rows continue into the
-// next row in memory, so in a tile that straddles N the lanes whose keys lie
-// past N get an offset beyond the descriptor. Keys read as zero K columns and
-// zero V rows have S = 0 and P = 1 and contribute nothing to W; they are
-// counted and removed from L. Query rows past M are zero and never stored.
+// ends at the last valid byte of batch b's rows from the tile on (or at zero
+// for tiles past the chunk end), so key rows past N and query rows past M read
+// zeros. In a head-dim-major K a row continues past key N into padding or the
+// next row, which the tile holding key N reads. That tile (and any tile past
+// the chunk) therefore has its scores masked: keys past the chunk end get
+// E = 0 whatever K held there. Query rows past M are never stored.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "mga_internal.h"
 
@@ -121,6 +130,14 @@ template <int HD>
 __device__ __forceinline__ int v_off(int key, int col_byte) {
     using G = Geo<HD>;
     return G::V_PART + key * G::V_ROW_BYTES + (((col_byte >> 5) ^ (key & 3)) << 5) + (col_byte & 31);
+}
+
+// Key-major K part: [32 keys][HD d] fp16, rows of HD/8 16-byte units; the
+// unit index is XORed with the key's low three bits, so that the eight keys
+// one ds_read_b128 pass serves hit eight distinct bank groups.
+template <int HD>
+__device__ __forceinline__ int km_off(int key, int col_byte) {
+    return key * (HD * 2) + (((col_byte >> 4) ^ (key & 7)) << 4) + (col_byte & 15);
 }
 
 template <int HD, int QT, int QW, int KS>
@@ -196,63 +213,61 @@ __device__ __forceinline__ void sync_tile() {
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 // Per-lane DMA offsets of this wave's share of a tile (independent of the
-// tile's position: the descriptor base moves instead). K instruction x fills
-// K rows 16 r .. 16 r + 15 (r = qw*PER + x), 4 lanes per 64-byte row; V
-// instruction x fills V rows V_RPI r .. V_RPI (r + 1) - 1, V_LPR lanes per
-// row. A lane fetches the 16-byte unit that the row's swizzle puts at its
+// tile's position: the descriptor base moves instead). Instruction x of the
+// wave fills 1 KiB of the K part and 1 KiB of the V part:
+//   * head-dim-major K: K rows 16 r .. 16 r + 15 (r = qw*PER + x), 4 lanes
+//     per 64-byte row of 32 keys;
+//   * key-major K and V: key rows V_RPI r .. V_RPI (r + 1) - 1, V_LPR lanes
+//     per row.
+// A lane fetches the 16-byte unit that the row's swizzle puts at its
 // position.
 template <int HD, int QW>
 struct TileDma {
     static constexpr int PER = Geo<HD>::DMA / QW;
-    uint32_t koff[PER];  // byte offset of the lane's 8 keys of head dim d from the tile's key 0
-    uint32_t kcol;       // first key of those 8, relative to the tile start
-    uint32_t voff;       // byte offset within the tile's 32 x HD V block (instruction 0)
+    uint32_t koff[PER];  // byte offset of the lane's K unit from the tile's key 0
+    uint32_t kcol;       // head-dim-major: first of the lane's 8 keys, relative to the tile
+    uint32_t voff[PER];  // byte offset of the lane's V unit from the tile's key 0
 };
-template <int HD, int QW>
-__device__ __forceinline__ TileDma<HD, QW> make_tile_dma(int qw, int lane, int N) {
+template <int HD, int QW, bool KM>
+__device__ __forceinline__ TileDma<HD, QW> make_tile_dma(int qw, int lane, int k_r, int v_n) {
     using G = Geo<HD>;
     constexpr int PER = G::DMA / QW;
     TileDma<HD, QW> t;
     const uint32_t lc = (lane & 3) ^ (((lane >> 3) & 1) << 1);  // bit 1 of d = bit 3 of lane
     t.kcol = 8 * lc;
+    const uint32_t kr = G::V_RPI * (qw * PER) + lane / G::V_LPR;  // key row of instruction 0
+    const uint32_t vc = (lane % G::V_LPR) ^ ((kr & 3) << 1);     // same for every x: V_RPI % 4 == 0
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-        const uint32_t d = 16 * (qw * PER + x) + (lane >> 2);
-        t.koff[x] = (d * (uint32_t)N + t.kcol) * 2;
+        if constexpr (KM) {
+            const uint32_t key = kr + x * G::V_RPI;
+            t.koff[x] = (key * (uint32_t)k_r + 8 * ((lane % G::V_LPR) ^ (key & 7))) * 2;
+        } else {
+            const uint32_t d = 16 * (qw * PER + x) + (lane >> 2);
+            t.koff[x] = (d * (uint32_t)k_r + t.kcol) * 2;
+        }
+        t.voff[x] = ((kr + x * G::V_RPI) * (uint32_t)v_n + 8 * vc) * 2;
     }
-    const uint32_t kr = G::V_RPI * (qw * PER) + lane / G::V_LPR;
-    const uint32_t vc = (lane % G::V_LPR) ^ ((kr & 3) << 1);
-    t.voff = (kr * HD + 8 * vc) * 2;
     return t;
 }
 
-// Issue this wave's DMA share of one stream's tile (keys key0 .. key0+31 of
-// the batch whose K and V arrays start at kb and vb) into the LDS tile at
-// byte address `lds`. `live` is false for tiles past the chunk end: their
-// descriptors hold zero records and the tile fills with zeros without
-// touching memory. The descriptors start at the tile and end with the batch.
+// Issue this wave's DMA share of one stream's tile into the LDS tile at byte
+// address `lds`. kp / vp point at the tile's first key in K and V; krec / vrec
+// are the byte extents from there to the batch's last valid byte. `live` is
+// false for a tile past the chunk end: its descriptors hold zero records and
+// the tile fills with zeros without touching memory. Key rows past N read
+// zeros; in a head-dim-major K a lane's 8 keys may run past N into the rest
+// of the row (or the next row), which the tail mask discards.
 template <int HD, int QW>
-__device__ __forceinline__ void issue_tile(const _Float16 *kb, const _Float16 *vb, int N, int key0,
+__device__ __forceinline__ void issue_tile(const _Float16 *kp, uint32_t krec, const _Float16 *vp, uint32_t vrec,
                                            bool live, uint32_t lds, int qw, const TileDma<HD, QW> &t) {
     constexpr int PER = Geo<HD>::DMA / QW;
-    const int rem = N - key0;  // keys from key0 to the end of the batch (> 0 when live)
-    const i32x4 kr = make_rsrc(kb + key0, live ? (uint32_t)(HD * N - key0) * 2 : 0u);
-    const i32x4 vr = make_rsrc(vb + (size_t)key0 * HD, live ? (uint32_t)rem * (HD * 2) : 0u);
-    const bool kin = (int)t.kcol < rem;
+    const i32x4 kr = make_rsrc(kp, live ? krec : 0u);
+    const i32x4 vr = make_rsrc(vp, live ? vrec : 0u);
 #pragma unroll
-    for (int x = 0; x < PER; ++x) dma16(kr, kin ? t.koff[x] : OOB, lds + (qw * PER + x) * 1024);
+    for (int x = 0; x < PER; ++x) dma16(kr, t.koff[x], lds + (qw * PER + x) * 1024);
 #pragma unroll
-    for (int x = 0; x < PER; ++x) dma16(vr, t.voff + x * 1024, lds + Geo<HD>::V_PART + (qw * PER + x) * 1024);
-}
-
-// Keys of a chunk of `len` keys that fall into this stream's first `nt` tiles
-// (tile it of stream ks starts at key (it*KS + ks)*32 of the chunk).
-template <int KS>
-__device__ __forceinline__ int live_keys(int len, int ks, int nt) {
-    const int full_tiles = len / KT, rem = len % KT;
-    int live = full_tiles > ks ? KT * cmin(nt, (full_tiles - ks + KS - 1) / KS) : 0;
-    if (rem != 0 && full_tiles >= ks && (full_tiles - ks) % KS == 0 && (full_tiles - ks) / KS < nt) live += rem;
-    return live;
+    for (int x = 0; x < PER; ++x) dma16(vr, t.voff[x], lds + Geo<HD>::V_PART + (qw * PER + x) * 1024);
 }
 
 // Returns the LDS byte offset x (< 2^18) unchanged, but the compiler must
@@ -272,14 +287,18 @@ __device__ __forceinline__ int opaque(int x) {
 // plus immediate offsets covers every read.
 template <int HD>
 struct LaneOffsets {
-    int k;                // K part, head dims 8h+jr (+4, +16 kk), keys 16 g1 + 4c
+    int k;                // head-dim-major K part, head dims 8h+jr (+4, +16 kk), keys 16 g1 + 4c
     int v[Geo<HD>::DT];   // V part, keys 4h+jr (+8, +16 t), head dims 32 dt + 16 g1 + 4c
+    int krow;             // key-major K part: byte offset of the lane's key row (key l % 32)
+    int kx;               // key-major K part: h ^ (key & 7); k-step kk reads unit 2 kk ^ kx
 };
 template <int HD>
 __device__ __forceinline__ LaneOffsets<HD> lane_offsets(int lane) {
     const int h = lane >> 5, g1 = (lane >> 4) & 1, jr = (lane & 15) >> 2, cb = 8 * (lane & 3);
     LaneOffsets<HD> r;
     r.k = k_off(8 * h + jr, 32 * g1 + cb);
+    r.krow = (lane & 31) * (HD * 2);
+    r.kx = h ^ (lane & 7);
 #pragma unroll
     for (int dt = 0; dt < Geo<HD>::DT; ++dt) r.v[dt] = v_off<HD>(4 * h + jr, 64 * dt + 32 * g1 + cb);
     return r;
@@ -292,6 +311,15 @@ __device__ __forceinline__ void read_k(const char *kb, half8 (&a)[Geo<HD>::KSTEP
 #pragma unroll
     for (int kk = 0; kk < Geo<HD>::KSTEPS; ++kk)
         a[kk] = cat8(tr_read(kb + kk * 16 * K_ROW_BYTES), tr_read(kb + kk * 16 * K_ROW_BYTES + 4 * K_ROW_BYTES));
+}
+// Key-major K: lane l needs key l % 32, head dims 16 kk + 8 h .. +7, i.e.
+// logical unit 2 kk + h of its row, stored at unit (2 kk + h) ^ (key & 7)
+// = 2 kk ^ kx.
+template <int HD>
+__device__ __forceinline__ void read_k_km(const char *tile, int krow, int kx, half8 (&a)[Geo<HD>::KSTEPS]) {
+#pragma unroll
+    for (int kk = 0; kk < Geo<HD>::KSTEPS; ++kk)
+        a[kk] = *reinterpret_cast<const half8 *>(tile + krow + (((2 * kk) ^ kx) << 4));
 }
 template <int HD>
 __device__ __forceinline__ void read_v(const char *const (&vb)[Geo<HD>::DT], half8 (&a)[2][Geo<HD>::DT]) {
@@ -321,8 +349,11 @@ __device__ __forceinline__ void scores(const half8 (&a)[Geo<HD>::KSTEPS],
 // register r of lane l holds key 8*(r/4) + 4*(l/32) + r%4 of query l%32, so
 // registers 8t..8t+7 are exactly the 8 k-slots of the second product's
 // B operand for keys 16t..16t+15.
-template <int QT>
-__device__ __forceinline__ void softmax(const float16v (&s)[QT], half8 (&p)[QT][2], float (&lsum)[QT][2]) {
+// With MASK, keys of the tile at or past `lim` (tile-relative) get E = 0:
+// register r holds key 8*(r/4) + 4*h + r%4, compared against lim - 4*h.
+template <int QT, bool MASK>
+__device__ __forceinline__ void softmax(const float16v (&s)[QT], half8 (&p)[QT][2], float (&lsum)[QT][2],
+                                        int lim_h) {
     const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -330,8 +361,13 @@ __device__ __forceinline__ void softmax(const float16v (&s)[QT], half8 (&p)[QT][
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float e0 = __builtin_amdgcn_exp2f(s[qt][8 * t + 2 * j]);
-                const float e1 = __builtin_amdgcn_exp2f(s[qt][8 * t + 2 * j + 1]);
+                const int r0 = 8 * t + 2 * j, r1 = r0 + 1;
+                float e0 = __builtin_amdgcn_exp2f(s[qt][r0]);
+                float e1 = __builtin_amdgcn_exp2f(s[qt][r1]);
+                if constexpr (MASK) {
+                    e0 = 8 * (r0 / 4) + r0 % 4 < lim_h ? e0 : 0.f;
+                    e1 = 8 * (r1 / 4) + r1 % 4 < lim_h ? e1 : 0.f;
+                }
                 const half2v hv = __builtin_convertvector(float2v{e0, e1}, half2v);
                 p[qt][t][2 * j] = hv[0];
                 p[qt][t][2 * j + 1] = hv[1];
@@ -354,11 +390,11 @@ __device__ __forceinline__ void pv(const half8 (&a)[2][Geo<HD>::DT], const half8
                 oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t][dt], p[qt][t], oacc[dt][qt], 0, 0, 0);
 }
 
-template <int HD, int QT, int QW, int KS>
+template <int HD, int QT, int QW, int KS, bool KM>
 __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const _Float16 *__restrict__ q, const _Float16 *__restrict__ k,
     const _Float16 *__restrict__ v, _Float16 *__restrict__ o, _Float16 *__restrict__ ws_o,
-    float *__restrict__ ws_l, int B, int M, int N, int chunk_keys, int nsplit, int mtiles) {
+    float *__restrict__ ws_l, mga::Strides st, int B, int M, int N, int chunk_keys, int nsplit, int mtiles) {
     using C = Cfg<HD, QT, QW, KS>;
     using G = Geo<HD>;
     constexpr int TILE_BYTES = G::TILE_BYTES, DT = G::DT, KSTEPS = G::KSTEPS;
@@ -383,12 +419,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const int qrow0 = mtile * C::ROWS;                     // first query row of the workgroup
     const int qbase = qrow0 + qw * 32 * QT;                // first query row of this wave
 
-    const _Float16 *kb = k + (size_t)b * HD * N;  // batch b's K [HD][N] and V [N][HD]
-    const _Float16 *vb = v + (size_t)b * N * HD;
+    const _Float16 *kb = k + b * st.k_b;  // batch b's K and V
+    const _Float16 *vb = v + b * st.v_b;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)(smem));
     const LaneOffsets<HD> lo = lane_offsets<HD>(lane);
-    const TileDma<HD, QW> td = make_tile_dma<HD, QW>(qw, lane, N);
+    const TileDma<HD, QW> td = make_tile_dma<HD, QW, KM>(qw, lane, st.k_r, st.v_n);
 
     // Tiles are numbered per stream: tile it of stream ks starts at chunk key
     // (it*KS + ks)*32. `ntiles` counts the tiles a stream visits.
@@ -396,17 +432,43 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const int ntiles = C::PRIVATE ? (chunk_tiles > ks ? (chunk_tiles - ks + KS - 1) / KS : 0)
                                   : (len + KS * KT - 1) / (KS * KT);
     auto tile_key = [&](int it) { return (it * KS + ks) * KT; };  // relative to kstart
-    auto issue = [&](int it, uint32_t lds) {
-        issue_tile<HD, QW>(kb, vb, N, kstart + tile_key(it), it < ntiles && tile_key(it) < len, lds, qw, td);
+    // Tile cursor of this stream: descriptor bases and byte extents of the
+    // next tile to issue. Tiles are issued in order, KS*32 keys apart, so the
+    // cursor advances by constant steps; `nlive` counts the stream's tiles
+    // that start inside the chunk.
+    const int key_first = kstart + ks * KT;
+    const int rem0 = N - key_first;  // > 0 whenever nlive > 0
+    const int nlive = len > ks * KT ? (len - ks * KT + KS * KT - 1) / (KS * KT) : 0;
+    const long long kstep = KM ? (long long)KS * KT * st.k_r : (long long)KS * KT;  // elements
+    const long long vstep = (long long)KS * KT * st.v_n;
+    const _Float16 *kcur = kb + (KM ? (long long)key_first * st.k_r : (long long)key_first);
+    const _Float16 *vcur = vb + (long long)key_first * st.v_n;
+    // Head-dim-major K: the extent ends with the 16-byte unit holding the
+    // batch's last key in row HD-1 (the unit lies in the row's storage, which
+    // starts 16-byte aligned), so a lane whose 8 keys straddle N reads its
+    // live keys whatever the granularity of the hardware's range check.
+    uint32_t krec = KM ? ((uint32_t)(rem0 - 1) * (uint32_t)st.k_r + HD) * 2
+                       : ((uint32_t)(HD - 1) * (uint32_t)st.k_r + (((uint32_t)rem0 + 7) & ~7u)) * 2;
+    uint32_t vrec = ((uint32_t)(rem0 - 1) * (uint32_t)st.v_n + HD) * 2;
+    const uint32_t krec_step = (uint32_t)kstep * 2, vrec_step = (uint32_t)vstep * 2;
+    auto issue = [&](int it, uint32_t lds) {  // called for it = 0, 1, 2, ... in order
+        issue_tile<HD, QW>(kcur, krec, vcur, vrec, it < nlive, lds, qw, td);
+        kcur += kstep;
+        vcur += vstep;
+        krec -= krec_step;
+        vrec -= vrec_step;
     };
 
-    // Q for the workgroup's rows -> LDS (rows past M read zero). Issued before
-    // any K/V tile so that the first step finds it.
+    // Q for the workgroup's rows -> LDS rows of HD*2 bytes (rows past M read
+    // zero). Issued before any K/V tile so that the first step finds it.
     {
+        constexpr int QLPR = HD / 8, QRPI = 64 / QLPR;  // lanes per row, rows per instruction
         const int qrows = min(C::ROWS, M - qrow0);
-        const i32x4 qr = make_rsrc(q + ((size_t)b * M + qrow0) * HD, (uint32_t)qrows * G::Q_ROW_BYTES);
+        const i32x4 qr = make_rsrc(q + b * st.q_b + (size_t)qrow0 * st.q_i,
+                                   ((uint32_t)(qrows - 1) * (uint32_t)st.q_i + HD) * 2);
+        const uint32_t lrow = lane / QLPR, lcol = 16 * (lane % QLPR);
         for (int j = wave; j < C::Q_OPS; j += C::NWAVES)
-            dma16(qr, (uint32_t)(j * 1024 + lane * 16), lds0 + C::Q_OFF + j * 1024);
+            dma16(qr, (j * QRPI + lrow) * (uint32_t)st.q_i * 2 + lcol, lds0 + C::Q_OFF + j * 1024);
     }
 
     float16v oacc[DT][QT];
@@ -438,6 +500,25 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         wait_lds();
     };
 
+    // Softmax numerators of a stream's last tile, the only one that can reach
+    // past the chunk end (the tile holding key N, or a tile wholly past the
+    // chunk): masked when it does. Every earlier tile of a stream ends before
+    // the next tile of the same stream starts, so it lies inside the chunk and
+    // takes the unmasked softmax, in a loop body without this branch.
+    auto softmax_last = [&](int it, const float16v (&sv)[QT], half8 (&pv_)[QT][2]) {
+        const int lim = len - tile_key(it);
+        if (lim >= KT)
+            softmax<QT, false>(sv, pv_, lsum, 0);
+        else
+            softmax<QT, true>(sv, pv_, lsum, lim - 4 * h);
+    };
+    auto load_k = [&](const char *tile, half8 (&a)[KSTEPS]) {
+        if constexpr (KM)
+            read_k_km<HD>(tile, opaque(lo.krow), lo.kx, a);
+        else
+            read_k<HD>(tile + opaque(lo.k), a);
+    };
+
     if constexpr (C::PRIVATE) {
         // Wave-private ring: buffers ring0 and ring0 + TILE_BYTES.
         const uint32_t ring0 = lds0 + wave * 2 * TILE_BYTES;
@@ -446,23 +527,29 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         issue(1, ring0 + TILE_BYTES);
         sync_tile<2 * C::TILE_OPS>();  // this wave's Q share landed; barrier: all of Q landed
         load_q();
-        for (int it = 0; it < ntiles; ++it) {
+        auto step = [&](int it, auto last) {
             wait_vm<C::TILE_OPS>();  // tile it landed (tile it+1 may still be in flight)
             const char *buf = ring + (it & 1) * TILE_BYTES;
             half8 ka[KSTEPS], va[2][DT];
             const char *vbase[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vbase[dt] = buf + lo.v[dt];
-            read_k<HD>(buf + lo.k, ka);
+            load_k(buf, ka);
             read_v<HD>(vbase, va);
             wait_lds();              // the buffer is free: refill it with tile it+2
             issue(it + 2, ring0 + (it & 1) * TILE_BYTES);
             float16v s[QT];
             half8 p[QT][2];
             scores<HD, QT>(ka, qf, s);
-            softmax<QT>(s, p, lsum);
+            if constexpr (decltype(last)::value)
+                softmax_last(it, s, p);
+            else
+                softmax<QT, false>(s, p, lsum, 0);
             pv<HD, QT>(va, p, oacc);
-        }
+        };
+        int it = 0;
+        for (; it + 1 < ntiles; ++it) step(it, std::false_type{});
+        if (it < ntiles) step(it, std::true_type{});
         wait_vm<0>();
         __syncthreads();  // every ring and the Q staging are free for the reduction
     } else {
@@ -497,10 +584,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         half8 p[QT][2];
         auto g1 = [&](int it, float16v (&sv)[QT]) {
             half8 a[KSTEPS];
-            read_k<HD>(tile_at(it) + opaque(lo.k), a);
+            load_k(tile_at(it), a);
             scores<HD, QT>(a, qf, sv);
         };
-        auto sm = [&](const float16v (&sv)[QT]) { softmax<QT>(sv, p, lsum); };
+        // Tiles before a stream's last (it <= niter - 2) lie inside the chunk.
+        auto sm = [&](const float16v (&sv)[QT]) { softmax<QT, false>(sv, p, lsum, 0); };
+        auto sm_last = [&](const float16v (&sv)[QT], int it) { softmax_last(it, sv, p); };
         auto g2 = [&](int it) {
             half8 a[2][DT];
             const char *vbase[DT];
@@ -514,23 +603,23 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         g1(0, s0);
         sync();                 // step 1 (tile 1 may lie past the chunk: zeros, unused)
         g1(1, s1);
-        sm(s0);
+        sm_last(s0, 0);         // tile 0 is the last one when niter == 1
         int it = 2;
         for (; it + 1 < niter; it += 2) {
             sync();
             g2(it - 2);
             g1(it, s0);
-            sm(s1);
+            sm(s1);             // tile it-1
             sync();
             g2(it - 1);
             g1(it + 1, s1);
-            sm(s0);
+            sm(s0);             // tile it
         }
         if (it < niter) {       // one more full step, it even
             sync();
             g2(it - 2);
             g1(it, s0);
-            sm(s1);
+            sm(s1);             // tile it-1
             ++it;
         }
         // Drain: tiles niter-2 and niter-1 still need their second product,
@@ -539,19 +628,15 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             g2(0);
         } else if (it & 1) {    // last step even: tile niter-1's scores in s0
             g2(niter - 2);
-            sm(s0);
+            sm_last(s0, niter - 1);
             g2(niter - 1);
         } else {                // last step odd: tile niter-1's scores in s1
             g2(niter - 2);
-            sm(s1);
+            sm_last(s1, niter - 1);
             g2(niter - 1);
         }
         sync_tile<0>();  // no DMA in flight, every wave done with the ring
     }
-
-    // Keys of this stream's tiles that lie outside the chunk or past N read
-    // as zeros and entered L as P = 1 each.
-    const float masked = (float)(KT * ntiles - live_keys<KS>(len, ks, ntiles));
 
     // Sum the KS streams of each query group in LDS (fixed order), then
     // write O (one split) or the partial W, L.
@@ -571,7 +656,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                                 oacc[dt][qt][4 * rb + 3]};
                 }
             const float mine = lsum[qt][0] + lsum[qt][1];
-            const float lfull = mine + __shfl_xor(mine, 32) - masked;
+            const float lfull = mine + __shfl_xor(mine, 32);
             if (h == 0) lreg[qr] = lfull;
         }
     }
@@ -600,7 +685,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         const int row = qbase + qr;
         if (row < M) {
             if (nsplit == 1) {
-                _Float16 *dst = o + ((size_t)b * M + row) * HD + d0;
+                _Float16 *dst = o + b * st.o_b + (size_t)row * st.o_i + d0;
 #pragma unroll
                 for (int x = 0; x < C::VPL; x += 4) {
                     half4 hv;
@@ -632,8 +717,8 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
 template <int HD>
 __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__restrict__ ws_o,
                                                           const float *__restrict__ ws_l,
-                                                          _Float16 *__restrict__ o, long long rows,
-                                                          int nsplit) {
+                                                          _Float16 *__restrict__ o, long long o_b, int o_i,
+                                                          int M, long long rows, int nsplit) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const long long row = gid / (HD / 4);
     const int c = (int)(gid % (HD / 4));
@@ -652,20 +737,28 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     half4 hv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(acc[i] / l);
-    *reinterpret_cast<half4 *>(o + row * HD + 4 * c) = hv;
+    const long long b = row / M;
+    *reinterpret_cast<half4 *>(o + b * o_b + (row - b * M) * o_i + 4 * c) = hv;
 }
 
-template <int HD, int QT, int QW, int KS>
-int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
-                       _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
+template <int HD, int QT, int QW, int KS, bool KM>
+int launch_partial_layout(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
+                          _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
     static_assert(32 * QT * QW == 32 || 32 * QT * QW == 64 || 32 * QT * QW == 128 || 32 * QT * QW == 256,
                   "rows per workgroup");
     const int pairs = p.B * p.splits;
     const int groups = (pairs + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.mtiles));
-    hipLaunchKernelGGL((gqa_partial_kernel<HD, QT, QW, KS>), grid, dim3(64 * QW * KS), 0, st, q, k, v, o,
-                       w, l, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles);
+    hipLaunchKernelGGL((gqa_partial_kernel<HD, QT, QW, KS, KM>), grid, dim3(64 * QW * KS), 0, st, q, k, v, o,
+                       w, l, p.st, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles);
     return (int)hipGetLastError();
+}
+
+template <int HD, int QT, int QW, int KS>
+int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
+                       _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
+    if (p.key_major) return launch_partial_layout<HD, QT, QW, KS, true>(p, q, k, v, o, w, l, st);
+    return launch_partial_layout<HD, QT, QW, KS, false>(p, q, k, v, o, w, l, st);
 }
 
 }  // namespace
@@ -707,10 +800,10 @@ int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
     const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
     if (p.D == 128)
         hipLaunchKernelGGL(gqa_combine_kernel<128>, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
-                           (_Float16 *)o, rows, p.splits);
+                           (_Float16 *)o, p.st.o_b, p.st.o_i, p.M, rows, p.splits);
     else
         hipLaunchKernelGGL(gqa_combine_kernel<64>, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
-                           (_Float16 *)o, rows, p.splits);
+                           (_Float16 *)o, p.st.o_b, p.st.o_i, p.M, rows, p.splits);
     return (int)hipGetLastError();
 }
 

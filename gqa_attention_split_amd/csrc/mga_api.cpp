@@ -71,7 +71,6 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 int make_plan(int B, int M, int N, int D, int splits, Plan *p) {
     if (B < 0 || M < 0 || N < 1 || splits < 0) return MGA_ERR_INVALID_VALUE;
     if (D != 64 && D != 128) return MGA_ERR_CONFIG;
-    if (N % 8 != 0) return MGA_ERR_LAYOUT;
     const long long nblocks = ceil_div(N, kKeyBlock);
     if (splits > nblocks) return MGA_ERR_CONFIG;
     p->B = B;
@@ -82,6 +81,8 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p) {
     p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;
+    p->key_major = false;
+    p->st = Strides{(long long)M * D, (long long)D * N, (long long)N * D, (long long)M * D, D, N, D, D};
     const int want = splits == 0 ? policy_splits(B, M, N, p->variant) : splits;
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
@@ -97,6 +98,49 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p) {
     } else {
         p->ws_bytes = 0;
     }
+    return MGA_OK;
+}
+
+int set_layout(Plan *p, const long long *s) {
+    const long long B = p->B, M = p->M, N = p->N, D = p->D;
+    long long q_b, q_i, k_b, k_d, k_n, v_b, v_n, o_b, o_i;
+    if (s) {
+        q_b = s[0], q_i = s[1], k_b = s[2], k_d = s[3], k_n = s[4];
+        v_b = s[5], v_n = s[6], o_b = s[7], o_i = s[8];
+    } else {
+        q_b = M * D, q_i = D, k_b = D * N, k_d = N, k_n = 1, v_b = N * D, v_n = D, o_b = M * D, o_i = D;
+    }
+    // Row strides up to 2^30 and batch strides up to 2^48 elements keep every
+    // product below 2^63; the byte extents are checked against 2^31 below.
+    const long long row_max = 1LL << 30, batch_max = 1LL << 48;
+    for (long long x : {q_b, q_i, k_b, k_d, k_n, v_b, v_n, o_b, o_i})
+        if (x < 0) return MGA_ERR_LAYOUT;
+    for (long long r : {q_i, k_d, k_n, v_n, o_i})
+        if (r > row_max) return MGA_ERR_CONFIG;
+    for (long long b : {q_b, k_b, v_b, o_b})
+        if (b > batch_max) return MGA_ERR_CONFIG;
+    // Every 16-byte DMA unit and output store stays aligned: strides other
+    // than the unit one are multiples of 8 elements.
+    auto al = [](long long x) { return x % 8 == 0; };
+    bool km;
+    if (k_n == 1 && k_d >= N && al(k_d))
+        km = false;  // K[d][n]: head-dim-major rows of at least N keys
+    else if (k_d == 1 && k_n >= D && al(k_n))
+        km = true;   // K[n][d]: key-major rows of at least D head dims
+    else
+        return MGA_ERR_LAYOUT;
+    if (!al(q_b) || !al(k_b) || !al(v_b) || !al(o_b)) return MGA_ERR_LAYOUT;
+    if (!al(q_i) || !al(v_n) || !al(o_i) || q_i < D || v_n < D || o_i < D) return MGA_ERR_LAYOUT;
+    if (B > 1 && M > 0 && o_b < (M - 1) * o_i + D) return MGA_ERR_LAYOUT;  // O batches overlap
+    // Byte extents behind one buffer descriptor: a batch's K and V from the
+    // first key on, and a workgroup's Q rows. A head-dim-major K descriptor
+    // ends at the 16-byte unit that holds key N - 1 of the last row.
+    const long long lim = 1LL << 31;
+    const long long k_ext = km ? (N - 1) * k_n + D : (D - 1) * k_d + ((N + 7) & ~7LL);
+    if (2 * k_ext >= lim || 2 * ((N - 1) * v_n + D) >= lim) return MGA_ERR_CONFIG;
+    if (2 * ((p->tile_rows - 1) * q_i + D) >= lim) return MGA_ERR_CONFIG;
+    p->key_major = km;
+    p->st = Strides{q_b, k_b, v_b, o_b, (int)q_i, (int)(km ? k_n : k_d), (int)v_n, (int)o_i};
     return MGA_OK;
 }
 
@@ -121,10 +165,11 @@ const char *mga_status_string(int status) {
     case MGA_ERR_INVALID_VALUE:
         return "MGA_ERR_INVALID_VALUE: null pointer, negative B/M/splits, or N < 1";
     case MGA_ERR_LAYOUT:
-        return "MGA_ERR_LAYOUT: pointer not 16-byte aligned or N not a multiple of 8";
+        return "MGA_ERR_LAYOUT: pointer not 16-byte aligned, or a stride not allowed (contiguous K "
+               "needs N to be a multiple of 8)";
     case MGA_ERR_CONFIG:
         return "MGA_ERR_CONFIG: head dim not 64 or 128, splits above ceil(N/128), N above 2^30/D - 1, "
-               "or a grid too large";
+               "a stride or byte extent too large, or a grid too large";
     case MGA_ERR_WORKSPACE: return "MGA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MGA_ERR_HIP: return "MGA_ERR_HIP: kernel launch failed";
     default: return "unknown mga status";
@@ -151,8 +196,16 @@ size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits) {
 
 int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o, int B, int M,
                        int N, int D, int splits, const void *ws, size_t ws_bytes) {
+    return mga_gqa_check_args_strided(q, k, v, o, B, M, N, D, nullptr, splits, ws, ws_bytes);
+}
+
+int mga_gqa_check_args_strided(const void *q, const void *k, const void *v, const void *o, int B,
+                               int M, int N, int D, const int64_t *strides, int splits,
+                               const void *ws, size_t ws_bytes) {
+    static_assert(sizeof(long long) == sizeof(int64_t), "stride width");
     mga::Plan p;
-    const int rc = mga::make_plan(B, M, N, D, splits, &p);
+    int rc = mga::make_plan(B, M, N, D, splits, &p);
+    if (rc == MGA_OK) rc = mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
     if (rc != MGA_OK) return rc;
     return mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
 }
@@ -161,6 +214,7 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o, int B,
                     int D, int splits, void *ws, size_t ws_bytes, void *stream) {
     mga::Plan p;
     int rc = mga::make_plan(B, M, N, D, splits, &p);
+    if (rc == MGA_OK) rc = mga::set_layout(&p, nullptr);
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0) return MGA_OK;
@@ -171,6 +225,7 @@ int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits, const void 
                     size_t ws_bytes, void *stream) {
     mga::Plan p;
     int rc = mga::make_plan(B, M, N, D, splits, &p);
+    if (rc == MGA_OK) rc = mga::set_layout(&p, nullptr);
     if (rc == MGA_OK) rc = mga::check_call(nullptr, nullptr, nullptr, o, p, ws, ws_bytes, false);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0 || p.splits == 1) return MGA_OK;
@@ -179,8 +234,15 @@ int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits, const void 
 
 int mga_gqa_forward(const void *q, const void *k, const void *v, void *o, int B, int M, int N,
                     int D, int splits, void *ws, size_t ws_bytes, void *stream) {
+    return mga_gqa_forward_strided(q, k, v, o, B, M, N, D, nullptr, splits, ws, ws_bytes, stream);
+}
+
+int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o, int B, int M,
+                            int N, int D, const int64_t *strides, int splits, void *ws,
+                            size_t ws_bytes, void *stream) {
     mga::Plan p;
     int rc = mga::make_plan(B, M, N, D, splits, &p);
+    if (rc == MGA_OK) rc = mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0) return MGA_OK;

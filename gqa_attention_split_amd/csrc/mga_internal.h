@@ -5,9 +5,20 @@
 
 namespace mga {
 
+// Element strides of one call. Q[b][i][d] at q + b*q_b + i*q_i + d,
+// V[b][n][d] at v + b*v_b + n*v_n + d, O[b][i][d] at o + b*o_b + i*o_i + d;
+// K[b][d][n] at k + b*k_b + d*k_r + n (head-dim-major) or k + b*k_b + n*k_r + d
+// (key-major). Row strides are below 2^30 (checked with the byte extents).
+struct Strides {
+    long long q_b, k_b, v_b, o_b;
+    int q_i, k_r, v_n, o_i;
+};
+
 // Geometry of one launch, decided on the host before anything is enqueued.
 struct Plan {
     int B, M, N, D;
+    bool key_major;   // K stored [N][D] per batch (else [D][N])
+    Strides st;
     int variant;      // kernel shape, one of the kVariant* values
     int tile_rows;    // query rows per workgroup
     int mtiles;       // ceil(M / tile_rows)
@@ -34,7 +45,13 @@ constexpr int max_keys(int D) { return (1 << 30) / D - 1; }
 constexpr int kThreads = 256;
 
 // Fills `p` for a call; returns an mga_status (0 = ok). Host only, no HIP calls.
+// The layout is left contiguous and unchecked; set_layout fixes it.
 int make_plan(int B, int M, int N, int D, int splits, Plan *p);
+
+// Checks the nine element strides (q_b, q_i, k_b, k_d, k_n, v_b, v_n, o_b,
+// o_i; NULL = contiguous) against the plan's shape and stores them. Returns
+// an mga_status.
+int set_layout(Plan *p, const long long *strides);
 
 // Argument checks shared by every entry point (host only).
 int check_call(const void *q, const void *k, const void *v, const void *o, const Plan &p,

@@ -19,15 +19,21 @@
  *     O = (sum_s L_s o_s) / (sum_s L_s),  o_s = W_s / L_s,
  *     W_s = sum_{n in split s} e_n V[n],  L_s = sum_{n in split s} e_n.
  *
- * Data layout (all row-major, contiguous, IEEE fp16, device memory):
+ * Data layout (IEEE fp16, device memory). The default entry points take
+ * row-major contiguous tensors, the graph inputs' default strides (kaispace
+ * blog, section 2: new_input records a shape and strides, row-major unless
+ * given, and compile() requires run-time tensors to match them):
  *     q [B][M][D]      query rows (axis 0 = batch x KV heads)
  *     k [B][D][N]      keys stored head-dim-major ("pre-transposed")
  *     v [B][N][D]      values
  *     o [B][M][D]      output, written with round-to-nearest-even
+ * mga_gqa_forward_strided takes the same logical tensors as strided views
+ * instead (see there), including K stored key-major.
  * The head dimension D is 64 (the tutorial graph) or 128 (the tutorial's
  * launch example: Q (64, 1, 128), K (64, 128, 4096), V (64, 4096, 128)).
- * Pointers must be 16-byte aligned and N a multiple of 8 (every K row then
- * starts on a 16-byte boundary); N is at most 2^30 / D - 1.
+ * Pointers must be 16-byte aligned; for contiguous K, N must be a multiple
+ * of 8 (every K row then starts on a 16-byte boundary). N is at most
+ * 2^30 / D - 1.
  *
  * Numerics: fp16 MFMA products with fp32 accumulation; E = exp(A) in fp32
  * via the hardware exp2 of log2(e) Q rounded to fp16; P = fp16(E), rounded to
@@ -54,6 +60,7 @@
 #define MGA_GQA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -105,8 +112,8 @@ size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
  * workgroup (D = 64: 32, 64, 128 or 256 -- the largest tile whose workgroups
  * still cover all 256 compute units without splitting, else 64, or 32 for
  * M <= 32; D = 128: 32) and the effective split count. Either output pointer
- * may be NULL. Returns the status mga_gqa_check_args would give for the shape
- * (MGA_OK, INVALID_VALUE, LAYOUT or CONFIG). */
+ * may be NULL. Returns MGA_OK, INVALID_VALUE or CONFIG for the shape; the
+ * memory layout is not part of the plan. */
 int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
 
 /* Host-only validation of a forward call; makes no HIP call and launches
@@ -119,11 +126,40 @@ int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *
 /* The whole path: partial kernel, then (when the effective split count is
  * above 1) the combine kernel, both on `stream`. splits = 0 lets the policy
  * choose. ws/ws_bytes: caller-owned device workspace of at least
- * mga_gqa_workspace_bytes(B, M, N, splits) bytes, 16-byte aligned. Calls
+ * mga_gqa_workspace_bytes(B, M, N, D, splits) bytes, 16-byte aligned. Calls
  * that share a workspace must not overlap in time. */
 int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
                     int B, int M, int N, int D, int splits, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* mga_gqa_forward on strided views: graph inputs declared with other strides
+ * (the same blog section: new_input accepts explicit strides), e.g. K as the
+ * transpose of a [keys][head dim] cache, or K and V interleaved in one cache. `strides` points to nine element strides
+ * (not bytes), in this order:
+ *     q_b, q_i          Q[b][i][d] at q + b*q_b + i*q_i + d
+ *     k_b, k_d, k_n     K[b][d][n] at k + b*k_b + d*k_d + n*k_n
+ *     v_b, v_n          V[b][n][d] at v + b*v_b + n*v_n + d
+ *     o_b, o_i          O[b][i][d] at o + b*o_b + i*o_i + d
+ * NULL means contiguous (the call is then mga_gqa_forward). Accepted
+ * layouts (else MGA_ERR_LAYOUT):
+ *   - K head-dim-major (k_n == 1, k_d >= N) or key-major (k_d == 1,
+ *     k_n >= D);
+ *   - every stride other than those unit strides a non-negative multiple of
+ *     8 elements, row strides q_i, v_n, o_i >= D, and O's batches disjoint
+ *     (o_b >= (M - 1) o_i + D when B > 1); Q, K and V may overlap or be
+ *     shared across batches (stride 0).
+ * N may then be any value from 1 to 2^30 / D - 1 (keys past N in a padded
+ * head-dim-major row are never used). Strides above 2^30 (rows) or 2^48
+ * (batches), or a batch's K or V, or a workgroup's Q rows, spanning 2^31
+ * bytes or more, give MGA_ERR_CONFIG. Same workspace as mga_gqa_forward. */
+int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o,
+                            int B, int M, int N, int D, const int64_t *strides, int splits,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Host-only validation of a mga_gqa_forward_strided call (no HIP call). */
+int mga_gqa_check_args_strided(const void *q, const void *k, const void *v, const void *o,
+                               int B, int M, int N, int D, const int64_t *strides, int splits,
+                               const void *ws, size_t ws_bytes);
 
 /* Only the split-KV partial kernel (the for-loop over keys). With one
  * effective split it writes O directly (normalised, fp16); otherwise it

@@ -154,3 +154,72 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         _lib.load()
+
+
+# ---------------------------------------------------------------- strides --
+_NAMES = ("q_b", "q_i", "k_b", "k_d", "k_n", "v_b", "v_n", "o_b", "o_i")
+
+
+def _st(B, M, N, D, **kw):
+    base = dict(q_b=M * D, q_i=D, k_b=D * N, k_d=N, k_n=1, v_b=N * D, v_n=D, o_b=M * D, o_i=D)
+    base.update(kw)
+    return [base[n] for n in _NAMES]
+
+
+def _check_st(B=2, M=256, N=4096, D=64, splits=1, strides="default", **kw):
+    st = _st(B, M, N, D, **kw) if strides == "default" else strides
+    return mga.mga_gqa_check_args_strided(A, A, A, A, B, M, N, D, st, splits, None, 0)
+
+
+def test_strided_layouts_accepted():
+    assert _check_st() == mga.MGA_OK
+    assert _check_st(strides=None) == mga.MGA_OK                      # NULL = contiguous
+    for D in (64, 128):
+        # K as the transpose of a (B, N, D) tensor: any N
+        for N in (1, 13, 1001, 4096):
+            assert _check_st(N=N, D=D, k_b=N * D, k_d=1, k_n=D) == mga.MGA_OK, (N, D)
+        # head-dim-major K rows padded to a multiple of 8 keys
+        assert _check_st(N=1001, D=D, k_b=D * 1008, k_d=1008) == mga.MGA_OK
+        # K and V interleaved in one (B, N, 2, D) cache; Q and O inside wider rows
+        assert _check_st(N=4096, D=D, k_b=4096 * 2 * D, k_d=1, k_n=2 * D, v_b=4096 * 2 * D,
+                         v_n=2 * D, q_i=3 * D, q_b=256 * 3 * D, o_i=2 * D, o_b=256 * 2 * D) == mga.MGA_OK
+    # K, V and Q shared by every batch (stride 0)
+    assert _check_st(q_b=0, k_b=0, v_b=0) == mga.MGA_OK
+    # O batches may sit anywhere when there is one batch
+    assert _check_st(B=1, o_b=8) == mga.MGA_OK
+
+
+def test_strided_layouts_rejected():
+    # contiguous head-dim-major K needs N % 8 == 0 (rows 16-byte aligned)
+    assert _check_st(N=1001, k_b=64 * 1001, k_d=1001) == mga.MGA_ERR_LAYOUT
+    assert _check_st(strides=None, N=1001) == mga.MGA_ERR_LAYOUT
+    assert _check_st(k_n=2) == mga.MGA_ERR_LAYOUT                      # no unit stride in K
+    assert _check_st(k_d=1, k_n=56) == mga.MGA_ERR_LAYOUT              # key rows shorter than D
+    assert _check_st(k_d=4088) == mga.MGA_ERR_LAYOUT                   # head-dim rows shorter than N
+    assert _check_st(k_d=1, k_n=68) == mga.MGA_ERR_LAYOUT              # not a multiple of 8
+    for name, val in (("q_i", 68), ("q_i", 56), ("v_n", 60), ("v_n", 56), ("o_i", 72 + 4),
+                      ("o_i", 32), ("q_b", 4), ("k_b", 12), ("v_b", 2), ("o_b", 16384 + 4)):
+        assert _check_st(**{name: val}) == mga.MGA_ERR_LAYOUT, (name, val)
+    for name in _NAMES:
+        assert _check_st(**{name: -8}) == mga.MGA_ERR_LAYOUT, name
+    # O batches must not overlap: (M - 1) * o_i + D = 16384
+    assert _check_st(o_b=16384) == mga.MGA_OK
+    assert _check_st(o_b=16376) == mga.MGA_ERR_LAYOUT
+    # byte extents behind one descriptor stay below 2^31
+    assert _check_st(k_d=1, k_n=1 << 18, k_b=0) == mga.MGA_OK          # (4095 * 2^18 + 64) * 2 < 2^31
+    assert _check_st(k_d=1, k_n=1 << 19, k_b=0) == mga.MGA_ERR_CONFIG
+    assert _check_st(v_n=1 << 19) == mga.MGA_ERR_CONFIG
+    assert _check_st(q_i=1 << 25) == mga.MGA_ERR_CONFIG                # 63 rows * 2^26 bytes (64-row tiles)
+    assert _check_st(q_i=1 << 24) == mga.MGA_OK                        # (63 * 2^24 + 64) * 2 < 2^31
+    assert _check_st(o_i=(1 << 30) + 8) == mga.MGA_ERR_CONFIG
+    assert _check_st(q_b=(1 << 48) + 8) == mga.MGA_ERR_CONFIG
+    # a layout error comes back from the strided forward without launching
+    assert mga.mga_gqa_forward_strided(A, A, A, A, 2, 256, 1001, 64, _st(2, 256, 1001, 64), 1,
+                                       None, 0, None) == mga.MGA_ERR_LAYOUT
+
+
+def test_plan_accepts_any_key_count():
+    # the plan and workspace do not depend on the layout, so N % 8 != 0 is fine there
+    rc, rows, eff = mga.mga_gqa_plan(2, 256, 1001, 64, 0)
+    assert rc == mga.MGA_OK and eff == mga.mga_gqa_effective_splits(2, 256, 1001, 64, 0)
+    assert mga.mga_gqa_workspace_bytes(2, 256, 1001, 64, 2) > 0
