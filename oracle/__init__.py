@@ -16,6 +16,18 @@ Graph" on the Mirage documentation page):
 Each takes the exact values of fp16 inputs (converted losslessly to float64)
 and returns O in float64. Pins (closed forms, invariants, a library witness and
 a high-precision brute force) live in ``tests/test_oracle_pins.py``.
+
+The QK-normalised variant (Mirage documentation tutorial "Implement QK
+Normalization and Optimize Attention Kernel in Python" / "Superoptimize
+Attention with QK Normalization": Q = rms_norm(Q), K = rms_norm(K), then the
+same five operations) is ``gqa_qknorm_f64``: ``rms_norm_f64`` on Q and K,
+then ``gqa_f64`` on the normalised values. The pages name rms_norm without
+its axis, eps or weight; the reading taken is the one the tutorial's stated
+purpose (QK normalisation as in Chameleon, i.e. per attention head vector)
+supports: every query row and every key vector (a column of the
+head-dim-major K) is divided by the root mean square of its D entries,
+eps = 1e-6 inside the square root, no weight. Its pins live in
+``tests/test_oracle_qknorm_pins.py``.
 """
 from __future__ import annotations
 
@@ -110,3 +122,22 @@ def gqa_numpy_f64(q, k, v) -> np.ndarray:
     S = E.sum(axis=2, keepdims=True)        # reduction(E, 2)    (B, M, 1)
     Dm = E / S                              # div(E, S)
     return np.matmul(Dm, v64)               # matmul(D, V)       (B, M, D)
+
+
+def rms_norm_f64(x, axis: int, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(mean(x^2 along `axis`) + eps) in float64, no weight: the
+    rms_norm step of the QK-normalised attention tutorial, applied to every
+    vector along `axis` (the head dim)."""
+    x64 = _as_f64(x)
+    ms = np.mean(x64 * x64, axis=axis, keepdims=True)
+    return x64 / np.sqrt(ms + eps)
+
+
+def gqa_qknorm_f64(q, k, v, eps: float = 1e-6) -> np.ndarray:
+    """Attention with QK normalisation in fp64: Q = rms_norm(Q) over each
+    query row's D entries, K = rms_norm(K) over each key's D entries (axis 1
+    of the head-dim-major K), then the GQA graph (gqa_f64) on those values.
+    The graph keeps no max subtraction; fp64 holds exp(A) for |A| <= D."""
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    _shapes(q64, k64, v64)
+    return gqa_f64(rms_norm_f64(q64, axis=2, eps=eps), rms_norm_f64(k64, axis=1, eps=eps), v64)
