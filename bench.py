@@ -57,6 +57,9 @@ def parse_args():
                     help="also run one plain device-to-device copy of known size "
                          "(reference dispatch for FETCH_SIZE / WRITE_SIZE scaling)")
     ap.add_argument("--eager", action="store_true", help="also time without graphs")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="time the QK-normalised variant (rms_norm of Q rows and key vectors, "
+                         "eps 1e-6) instead of the plain graph")
     return ap.parse_args()
 
 
@@ -171,9 +174,13 @@ def main():
     base = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
     sets = [base] + [[t.clone() for t in base] for _ in range(R - 1)]
     outs = [torch.empty((B, M, D), dtype=torch.float16, device=dev) for _ in range(R)]
-    splits = args.splits if args.splits > 0 else mga.mga_gqa_choose_splits(B, M, N, D)
-    eff = mga.mga_gqa_effective_splits(B, M, N, D, splits)
-    ws = mga.workspace_for(B, M, N, D, splits, device=dev)
+    if args.qk_norm:
+        splits = args.splits
+        eff = mga.mga_gqa_qknorm_plan(B, M, N, D, splits)[2]
+    else:
+        splits = args.splits if args.splits > 0 else mga.mga_gqa_choose_splits(B, M, N, D)
+        eff = mga.mga_gqa_effective_splits(B, M, N, D, splits)
+    ws = mga.workspace_for(B, M, N, D, splits, device=dev, qk_norm=args.qk_norm)
     ws_ptr = 0 if ws is None else ws.data_ptr()
     ws_bytes = 0 if ws is None else ws.numel()
     lib = mga._lib.load()
@@ -184,7 +191,11 @@ def main():
 
     def fwd(i, rotate=True):
         j = i % R if rotate else 0
-        rc = lib.mga_gqa_forward(*ptrs[j], optr[j], B, M, N, D, splits, ws_ptr, ws_bytes, sh)
+        if args.qk_norm:
+            rc = lib.mga_gqa_qknorm_forward(*ptrs[j], optr[j], B, M, N, D, 1e-6, None, splits, ws_ptr,
+                                            ws_bytes, sh)
+        else:
+            rc = lib.mga_gqa_forward(*ptrs[j], optr[j], B, M, N, D, splits, ws_ptr, ws_bytes, sh)
         if rc:
             raise mga.GqaError(rc)
 
@@ -215,9 +226,12 @@ def main():
         timed_steps = args.steps if args.mode == "eager" else \
             max(1, math.ceil(args.steps / gsteps)) * gsteps
         print(f"[bench] forward {ms_step * 1e3:.3f} us/step", file=sys.stderr, flush=True)
-        ms_partial = timed(partial)
-        print(f"[bench] partial kernel {ms_partial * 1e3:.3f} us/launch", file=sys.stderr, flush=True)
-        ms_combine = timed(combine) if eff > 1 else 0.0
+        if args.qk_norm:  # no separate entry points: the pair is timed as one
+            ms_partial, ms_combine = ms_step, 0.0
+        else:
+            ms_partial = timed(partial)
+            print(f"[bench] partial kernel {ms_partial * 1e3:.3f} us/launch", file=sys.stderr, flush=True)
+            ms_combine = timed(combine) if eff > 1 else 0.0
         ms_hot = timed(lambda i: fwd(i, rotate=False))
         ms_eager = time_eager(torch, stream, fwd, args.steps, args.warmup) \
             if args.eager and args.mode == "graph" else None
@@ -258,7 +272,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "M": M, "N": N, "D": cfg.D,
                    "q_k_std": cfg.qk_std, "v_dist": cfg.v_dist, "seed": cfg.seed,
-                   "splits": eff, "rotating_sets": R,
+                   "splits": eff, "rotating_sets": R, "qk_norm": bool(args.qk_norm),
                    "timing": ("hip-graph replay" if args.mode == "graph" else "eager launches")
                    + ", events on the launch stream"},
         "hbm_gbps": round(gbps, 1),
@@ -268,8 +282,10 @@ def main():
         "partial_kernel_ms": round(ms_partial, 6),
         "combine_kernel_ms": round(ms_combine, 6),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": read_traffic(cfg.name),
-                     "kernel": "gqa_partial_kernel"},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": None if args.qk_norm else read_traffic(cfg.name),
+                     "kernel": "gqa_partial_kernel + gqa_combine_kernel (QK norm)" if args.qk_norm
+                     else "gqa_partial_kernel"},
     }
     if ms_eager is not None:
         result["eager_ms_per_step"] = round(ms_eager, 6)

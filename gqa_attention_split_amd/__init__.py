@@ -107,6 +107,30 @@ def mga_gqa_check_args_strided(q, k, v, o, B, M, N, D, strides, splits, ws, ws_b
                                                   _strides(strides), splits, _ptr(ws), ws_bytes)
 
 
+def mga_gqa_qknorm_forward(q, k, v, o, B, M, N, D, eps, strides, splits, ws, ws_bytes, stream) -> int:
+    return _lib.load().mga_gqa_qknorm_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D,
+                                              float(eps), _strides(strides), splits, _ptr(ws),
+                                              ws_bytes, _stream(stream))
+
+
+def mga_gqa_qknorm_workspace_bytes(B: int, M: int, N: int, D: int, splits: int) -> int:
+    return _lib.load().mga_gqa_qknorm_workspace_bytes(B, M, N, D, splits)
+
+
+def mga_gqa_qknorm_plan(B: int, M: int, N: int, D: int, splits: int):
+    """(status, tile_rows, effective_splits) of the QK-normalised path."""
+    import ctypes
+    rows, eff = ctypes.c_int(0), ctypes.c_int(0)
+    rc = _lib.load().mga_gqa_qknorm_plan(B, M, N, D, splits, ctypes.byref(rows), ctypes.byref(eff))
+    return rc, rows.value, eff.value
+
+
+def mga_gqa_qknorm_check_args(q, k, v, o, B, M, N, D, eps, strides, splits, ws, ws_bytes) -> int:
+    return _lib.load().mga_gqa_qknorm_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D,
+                                                 float(eps), _strides(strides), splits, _ptr(ws),
+                                                 ws_bytes)
+
+
 def mga_gqa_partial(q, k, v, o, B, M, N, D, splits, ws, ws_bytes, stream) -> int:
     return _lib.load().mga_gqa_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D, splits,
                                        _ptr(ws), ws_bytes, _stream(stream))
@@ -140,21 +164,25 @@ def _check_tensors(q, k, v):
     return B, M, N, D
 
 
-def workspace_for(B: int, M: int, N: int, D: int, splits: int = 0, device=None):
-    """A torch uint8 workspace of mga_gqa_workspace_bytes(...) bytes (or None)."""
+def workspace_for(B: int, M: int, N: int, D: int, splits: int = 0, device=None, qk_norm=False):
+    """A torch uint8 workspace of mga_gqa_workspace_bytes(...) (or, with
+    qk_norm, mga_gqa_qknorm_workspace_bytes(...)) bytes, or None."""
     import torch
-    nbytes = mga_gqa_workspace_bytes(B, M, N, D, splits)
+    nbytes = (mga_gqa_qknorm_workspace_bytes if qk_norm else mga_gqa_workspace_bytes)(B, M, N, D, splits)
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None):
+def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None,
+                qk_norm: bool = False, eps: float = 1e-6):
     """O = (exp(QK) / rowsum) V for fp16 GPU tensors q (B,M,D), k (B,D,N), v (B,N,D).
 
     The tensors may be strided views (the library checks which layouts it
     takes: unit stride along D for q, v and out; k with unit stride along N
-    or along D; other strides multiples of 8). ``out`` may be a view too."""
+    or along D; other strides multiples of 8). ``out`` may be a view too.
+    With ``qk_norm`` every query row and key vector is first rms-normalised
+    over the head dim (eps inside the root, no weight)."""
     import torch
     B, M, N, D = _check_tensors(q, k, v)
     if out is None:
@@ -162,18 +190,24 @@ def gqa_forward(q, k, v, out=None, splits: int = 0, workspace=None, stream=None)
     elif out.dtype != torch.float16 or tuple(out.shape) != (B, M, D) or out.device != q.device:
         raise ValueError(f"out must be a float16 (B, M, {D}) tensor on q's device")
     if workspace is None:
-        workspace = workspace_for(B, M, N, D, splits, q.device)
+        workspace = workspace_for(B, M, N, D, splits, q.device, qk_norm=qk_norm)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    if all(t.is_contiguous() for t in (q, k, v, out)):
-        rc = mga_gqa_forward(q, k, v, out, B, M, N, D, splits, workspace, ws_bytes, stream)
-    else:
+    contiguous = all(t.is_contiguous() for t in (q, k, v, out))
+    st = None
+    if not contiguous:
         for name, t in (("q", q), ("v", v), ("out", out)):
             if t.stride(2) != 1 and t.shape[2] > 1:
                 raise ValueError(f"{name} needs unit stride along the head dim")
         st = (q.stride(0), q.stride(1), k.stride(0), k.stride(1), k.stride(2), v.stride(0),
               v.stride(1), out.stride(0), out.stride(1))
+    if qk_norm:
+        rc = mga_gqa_qknorm_forward(q, k, v, out, B, M, N, D, eps, st, splits, workspace, ws_bytes,
+                                    stream)
+    elif contiguous:
+        rc = mga_gqa_forward(q, k, v, out, B, M, N, D, splits, workspace, ws_bytes, stream)
+    else:
         rc = mga_gqa_forward_strided(q, k, v, out, B, M, N, D, st, splits, workspace, ws_bytes, stream)
     if rc != MGA_OK:
         raise GqaError(rc)

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libmga_gqa.so")
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _S = ctypes.c_size_t
+_F = ctypes.c_float
 SIGNATURES = {
     "mga_status_string": ([_I], ctypes.c_char_p),
     "mga_gqa_choose_splits": ([_I, _I, _I, _I], _I),
@@ -27,6 +28,10 @@ SIGNATURES = {
     "mga_gqa_combine": ([_P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
     "mga_gqa_forward_strided": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _S, _P], _I),
     "mga_gqa_check_args_strided": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _S], _I),
+    "mga_gqa_qknorm_forward": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _P, _S, _P], _I),
+    "mga_gqa_qknorm_workspace_bytes": ([_I, _I, _I, _I, _I], _S),
+    "mga_gqa_qknorm_plan": ([_I, _I, _I, _I, _I, _P, _P], _I),
+    "mga_gqa_qknorm_check_args": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _P, _S], _I),
 }
 
 _lib = None

@@ -140,7 +140,7 @@ __device__ __forceinline__ int km_off(int key, int col_byte) {
     return key * (HD * 2) + (((col_byte >> 4) ^ (key & 7)) << 4) + (col_byte & 15);
 }
 
-template <int HD, int QT, int QW, int KS>
+template <int HD, int QT, int QW, int KS, bool QKN = false>
 struct Cfg {
     using G = Geo<HD>;
     static constexpr int TILE_BYTES = G::TILE_BYTES;
@@ -162,8 +162,14 @@ struct Cfg {
     static constexpr int Q_BYTES = ROWS * G::Q_ROW_BYTES;
     static constexpr int Q_OFF = PRIVATE ? RING_BYTES : DIST * STAGE_BYTES;
     static constexpr int Q_OPS = Q_BYTES / 1024;  // 1 KiB DMA instructions for the workgroup's Q
-    static constexpr int RED_BYTES = 32 * QT * G::RED_ROW_BYTES + 32 * QT * 4;  // one wave's epilogue region
-    static constexpr int LDS_BYTES = cmax(cmax(RING_BYTES, Q_OFF + Q_BYTES), NWAVES * RED_BYTES);
+    // One wave's epilogue region: its W rows (fp32), L per row, and with QK
+    // normalisation the running maximum per row.
+    static constexpr int RED_BYTES = 32 * QT * G::RED_ROW_BYTES + 32 * QT * 4 * (QKN ? 2 : 1);
+    // QK normalisation: 128 bytes per wave to move key scales between lanes.
+    static constexpr int SCR_BYTES = QKN ? NWAVES * 128 : 0;
+    static constexpr int SCR_OFF = cmax(cmax(RING_BYTES, Q_OFF + Q_BYTES), NWAVES * RED_BYTES);
+    static constexpr int LDS_BYTES = SCR_OFF + SCR_BYTES;
+    static_assert(!QKN || PRIVATE, "QK normalisation runs on the wave-private ring");
     static constexpr int DW = HD / KS;                // head dims each wave finalises
     static constexpr int VPL = 32 * QT * DW / 64;     // values per lane in the final write
     static_assert(PRIVATE || STAGES >= 5, "shared ring depth");
@@ -377,6 +383,63 @@ __device__ __forceinline__ void softmax(const float16v (&s)[QT], half8 (&p)[QT][
     }
 }
 
+// QK-normalised softmax numerators of one tile. Scores S = Q K arrive from raw
+// Q and K (exact fp16 products, fp32 sums); a = S * rk * rq - m is the
+// log2-domain normalised score of each key (rk: the key's 1/rms in
+// accumulator layout; rq: log2(e) / rms of the lane's query row) relative to
+// the row's reference maximum m. The normalised scores reach
+// |a| <= D log2(e), far past fp16 for exp, so the row keeps a reference m
+// (FlashAttention's running maximum, applied lazily): when a tile's largest
+// score exceeds m by more than 8, or the row has no reference yet, m moves to
+// that score and W, L are rescaled by 2^(m_old - m_new). P = fp16(2^a) then
+// stays below 2^8. Both lanes of a query (l, l+32) hold the same m.
+template <int DT, int QT, bool MASK>
+__device__ __forceinline__ void softmax_qkn(const float16v (&s)[QT], const float16v &rk, const float (&rq)[QT],
+                                            half8 (&p)[QT][2], float (&lsum)[QT][2], float (&m)[QT],
+                                            bool (&real)[QT], float16v (&oacc)[DT][QT], int lim_h) {
+    constexpr float TH = 8.f;
+    const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        float a[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            a[r] = __builtin_fmaf(s[qt][r] * rk[r], rq[qt], -m[qt]);
+            if constexpr (MASK) a[r] = 8 * (r / 4) + r % 4 < lim_h ? a[r] : -__builtin_inff();
+        }
+        float mx = a[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, a[r]);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const bool need = mx > TH || (!real[qt] && mx > -__builtin_inff());
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float delta = need ? mx : 0.f;
+            // A row without a reference has W = L = 0: scale by 0, not 2^-delta.
+            const float sc = need ? (real[qt] ? __builtin_amdgcn_exp2f(-delta) : 0.f) : 1.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= sc;
+            lsum[qt][0] *= sc;
+            lsum[qt][1] *= sc;
+            m[qt] += delta;
+            real[qt] = real[qt] || need;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[r] -= delta;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e0 = __builtin_amdgcn_exp2f(a[8 * t + 2 * j]);
+                const float e1 = __builtin_amdgcn_exp2f(a[8 * t + 2 * j + 1]);
+                const half2v hv = __builtin_convertvector(float2v{e0, e1}, half2v);
+                p[qt][t][2 * j] = hv[0];
+                p[qt][t][2 * j + 1] = hv[1];
+                lsum[qt][t] = __builtin_amdgcn_fdot2(hv, ones, lsum[qt][t], false);
+            }
+        }
+    }
+}
+
 // Second product of one tile: O^T += V^T P^T.
 template <int HD, int QT>
 __device__ __forceinline__ void pv(const half8 (&a)[2][Geo<HD>::DT], const half8 (&p)[QT][2],
@@ -390,12 +453,13 @@ __device__ __forceinline__ void pv(const half8 (&a)[2][Geo<HD>::DT], const half8
                 oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t][dt], p[qt][t], oacc[dt][qt], 0, 0, 0);
 }
 
-template <int HD, int QT, int QW, int KS, bool KM>
+template <int HD, int QT, int QW, int KS, bool KM, bool QKN>
 __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     const _Float16 *__restrict__ q, const _Float16 *__restrict__ k,
     const _Float16 *__restrict__ v, _Float16 *__restrict__ o, _Float16 *__restrict__ ws_o,
-    float *__restrict__ ws_l, mga::Strides st, int B, int M, int N, int chunk_keys, int nsplit, int mtiles) {
-    using C = Cfg<HD, QT, QW, KS>;
+    float *__restrict__ ws_l, mga::Strides st, int B, int M, int N, int chunk_keys, int nsplit, int mtiles,
+    float eps) {
+    using C = Cfg<HD, QT, QW, KS, QKN>;
     using G = Geo<HD>;
     constexpr int TILE_BYTES = G::TILE_BYTES, DT = G::DT, KSTEPS = G::KSTEPS;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -485,19 +549,77 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     // head dims 16*kk + 8*h .. +7, pre-scaled by log2(e) (fp32 product rounded
     // to fp16) so that the first product yields log2-domain scores and
     // E = exp2(S) needs no per-score multiply.
+    // With QK normalisation Q stays unscaled (exact in the first product, whose
+    // scores reach |D| after normalisation, where an fp16 rounding of the
+    // scaled Q would show); rq gets log2(e) / rms of the lane's query row, the
+    // sum of squares taken in fp32 over the lane's D/2 entries and its partner
+    // lane's (l ^ 32).
+    [[maybe_unused]] float rq[QT];
     auto load_q = [&]() {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const char *row = smem + C::Q_OFF + (qbase - qrow0 + 32 * qt + (lane & 31)) * G::Q_ROW_BYTES + 16 * h;
+            half8 x[KSTEPS];
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                half8 x = *reinterpret_cast<const half8 *>(row + 32 * kk);
+            for (int kk = 0; kk < KSTEPS; ++kk) x[kk] = *reinterpret_cast<const half8 *>(row + 32 * kk);
+            if constexpr (QKN) {
+                float ss = 0.f;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = (_Float16)((float)x[j] * LOG2E);
-                qf[qt][kk] = x;
+                for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2) {
+                        const half2v pr = {x[kk][j], x[kk][j + 1]};
+                        ss = __builtin_amdgcn_fdot2(pr, pr, ss, false);
+                    }
+                ss += __shfl_xor(ss, 32);
+                rq[qt] = LOG2E * __builtin_amdgcn_rsqf(ss * (1.f / HD) + eps);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[kk][j] = (_Float16)((float)x[kk][j] * LOG2E);
             }
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) qf[qt][kk] = x[kk];
         }
         wait_lds();
+    };
+
+    // QK normalisation: 1/rms of each key of a tile, in the accumulator layout
+    // of the scores (register r of lane l <-> key 8(r/4) + 4(l/32) + r%4). The
+    // sum of squares comes in fp32 from the K^T operand (lane l: key l%32, D/2
+    // entries; partner lane l ^ 32 the rest), then goes through this wave's
+    // 32-float LDS slot to the lanes that hold the key's scores.
+    [[maybe_unused]] float m_run[QT];
+    [[maybe_unused]] bool real[QT];
+    if constexpr (QKN) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            m_run[qt] = 0.f;
+            real[qt] = false;
+        }
+    }
+    auto key_scales = [&](const half8 (&ka)[KSTEPS], float16v &rk) {
+        float ss = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                const half2v pr = {ka[kk][j], ka[kk][j + 1]};
+                ss = __builtin_amdgcn_fdot2(pr, pr, ss, false);
+            }
+        ss += __shfl_xor(ss, 32);
+        const float r = __builtin_amdgcn_rsqf(ss * (1.f / HD) + eps);
+        float *slot = reinterpret_cast<float *>(smem + C::SCR_OFF + wave * 128);
+        if (h == 0) slot[lane & 31] = r;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4v t = *reinterpret_cast<const float4v *>(slot + 8 * g + 4 * h);
+            rk[4 * g] = t[0];
+            rk[4 * g + 1] = t[1];
+            rk[4 * g + 2] = t[2];
+            rk[4 * g + 3] = t[3];
+        }
     };
 
     // Softmax numerators of a stream's last tile, the only one that can reach
@@ -541,10 +663,19 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             float16v s[QT];
             half8 p[QT][2];
             scores<HD, QT>(ka, qf, s);
-            if constexpr (decltype(last)::value)
+            if constexpr (QKN) {
+                float16v rk;
+                key_scales(ka, rk);
+                const int lim = len - tile_key(it);
+                if (decltype(last)::value && lim < KT)
+                    softmax_qkn<DT, QT, true>(s, rk, rq, p, lsum, m_run, real, oacc, lim - 4 * h);
+                else
+                    softmax_qkn<DT, QT, false>(s, rk, rq, p, lsum, m_run, real, oacc, 0);
+            } else if constexpr (decltype(last)::value) {
                 softmax_last(it, s, p);
-            else
+            } else {
                 softmax<QT, false>(s, p, lsum, 0);
+            }
             pv<HD, QT>(va, p, oacc);
         };
         int it = 0;
@@ -658,6 +789,8 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             const float mine = lsum[qt][0] + lsum[qt][1];
             const float lfull = mine + __shfl_xor(mine, 32);
             if (h == 0) lreg[qr] = lfull;
+            if constexpr (QKN)  // a stream with no key in the row has no reference: -inf
+                if (h == 0) lreg[32 * QT + qr] = real[qt] ? m_run[qt] : -__builtin_inff();
         }
     }
     __syncthreads();
@@ -668,19 +801,41 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
 #pragma unroll
         for (int x = 0; x < C::VPL; ++x) acc[x] = 0.f;
         float l = 0.f;
+        // QK normalisation: the streams' W and L are relative to their own
+        // reference maxima; bring them to the largest, mstar, first.
+        [[maybe_unused]] float mstar = -__builtin_inff();
+        if constexpr (QKN) {
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+                const float *lreg = (const float *)(smem + (qw * KS + s2) * C::RED_BYTES + 32 * QT * G::RED_ROW_BYTES);
+                mstar = __builtin_fmaxf(mstar, lreg[32 * QT + qr]);
+            }
+        }
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
             const char *reg = smem + (qw * KS + s2) * C::RED_BYTES;
             const float *lreg = (const float *)(reg + 32 * QT * G::RED_ROW_BYTES);
+            if constexpr (QKN) {
+                const float ms = lreg[32 * QT + qr];
+                const float f = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - mstar) : 0.f;
 #pragma unroll
-            for (int x = 0; x < C::VPL; x += 4) {
-                const float4v t = *(const float4v *)(reg + qr * G::RED_ROW_BYTES + (d0 + x) * 4);
-                acc[x] += t[0];
-                acc[x + 1] += t[1];
-                acc[x + 2] += t[2];
-                acc[x + 3] += t[3];
+                for (int x = 0; x < C::VPL; x += 4) {
+                    const float4v t = *(const float4v *)(reg + qr * G::RED_ROW_BYTES + (d0 + x) * 4);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) acc[x + y] = __builtin_fmaf(f, t[y], acc[x + y]);
+                }
+                l = __builtin_fmaf(f, lreg[qr], l);
+            } else {
+#pragma unroll
+                for (int x = 0; x < C::VPL; x += 4) {
+                    const float4v t = *(const float4v *)(reg + qr * G::RED_ROW_BYTES + (d0 + x) * 4);
+                    acc[x] += t[0];
+                    acc[x + 1] += t[1];
+                    acc[x + 2] += t[2];
+                    acc[x + 3] += t[3];
+                }
+                l += lreg[qr];
             }
-            l += lreg[qr];
         }
         const int row = qbase + qr;
         if (row < M) {
@@ -696,6 +851,8 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             } else {
                 // Normalised partial: o_s = fp16(W_s / L_s), L_s in fp32 (0 when
                 // no weight survived fp16, so that it drops out of the combine).
+                // With QK normalisation W_s, L_s are relative to 2^mstar, so the
+                // workspace gets lse_s = mstar + log2(L_s) instead of L_s.
                 const size_t prow = ((size_t)split * B + b) * M + row;
                 _Float16 *dst = ws_o + prow * HD + d0;
                 const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -706,7 +863,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                     for (int y = 0; y < 4; ++y) hv[y] = (_Float16)(acc[x + y] * inv);
                     *(half4 *)(dst + x) = hv;
                 }
-                if (ks == 0 && d0 == 0) ws_l[prow] = l;
+                if (ks == 0 && d0 == 0) {
+                    if constexpr (QKN)
+                        ws_l[prow] = mstar + __builtin_log2f(l);
+                    else
+                        ws_l[prow] = l;
+                }
             }
         }
     }
@@ -714,7 +876,9 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
 
 // Combine: HD/4 threads per output row, 4 head dims each.
 // O = fp16(sum_s L_s o_s / sum_s L_s), both sums in split order.
-template <int HD>
+// With LSE (QK normalisation) the workspace holds lse_s = log2 of each
+// split's weight mass; the weights are then 2^(lse_s - max_s lse_s).
+template <int HD, bool LSE>
 __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__restrict__ ws_o,
                                                           const float *__restrict__ ws_l,
                                                           _Float16 *__restrict__ o, long long o_b, int o_i,
@@ -725,10 +889,14 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     if (row >= rows) return;
     float l = 0.f;
     float4v acc = {0.f, 0.f, 0.f, 0.f};
+    [[maybe_unused]] float lmax = -__builtin_inff();
+    if constexpr (LSE)
+        for (int s = 0; s < nsplit; ++s) lmax = __builtin_fmaxf(lmax, ws_l[(long long)s * rows + row]);
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
         const long long prow = (long long)s * rows + row;
-        const float ls = ws_l[prow];
+        float ls = ws_l[prow];
+        if constexpr (LSE) ls = ls > -__builtin_inff() ? __builtin_amdgcn_exp2f(ls - lmax) : 0.f;
         const half4 os = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
         l += ls;
 #pragma unroll
@@ -741,7 +909,7 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     *reinterpret_cast<half4 *>(o + b * o_b + (row - b * M) * o_i + 4 * c) = hv;
 }
 
-template <int HD, int QT, int QW, int KS, bool KM>
+template <int HD, int QT, int QW, int KS, bool KM, bool QKN>
 int launch_partial_layout(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
                           _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
     static_assert(32 * QT * QW == 32 || 32 * QT * QW == 64 || 32 * QT * QW == 128 || 32 * QT * QW == 256,
@@ -749,16 +917,16 @@ int launch_partial_layout(const mga::Plan &p, const _Float16 *q, const _Float16 
     const int pairs = p.B * p.splits;
     const int groups = (pairs + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.mtiles));
-    hipLaunchKernelGGL((gqa_partial_kernel<HD, QT, QW, KS, KM>), grid, dim3(64 * QW * KS), 0, st, q, k, v, o,
-                       w, l, p.st, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles);
+    hipLaunchKernelGGL((gqa_partial_kernel<HD, QT, QW, KS, KM, QKN>), grid, dim3(64 * QW * KS), 0, st, q, k, v,
+                       o, w, l, p.st, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles, p.eps);
     return (int)hipGetLastError();
 }
 
-template <int HD, int QT, int QW, int KS>
+template <int HD, int QT, int QW, int KS, bool QKN = false>
 int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
                        _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
-    if (p.key_major) return launch_partial_layout<HD, QT, QW, KS, true>(p, q, k, v, o, w, l, st);
-    return launch_partial_layout<HD, QT, QW, KS, false>(p, q, k, v, o, w, l, st);
+    if (p.key_major) return launch_partial_layout<HD, QT, QW, KS, true, QKN>(p, q, k, v, o, w, l, st);
+    return launch_partial_layout<HD, QT, QW, KS, false, QKN>(p, q, k, v, o, w, l, st);
 }
 
 }  // namespace
@@ -781,6 +949,14 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
     hipStream_t st = (hipStream_t)stream;
     const _Float16 *qh = (const _Float16 *)q, *kh = (const _Float16 *)k, *vh = (const _Float16 *)v;
     _Float16 *oh = (_Float16 *)o;
+    if (p.qknorm) {
+        switch (p.variant) {
+        case kVariantDecode: return launch_partial_cfg<64, 1, 1, 8, true>(p, qh, kh, vh, oh, w, l, st);
+        case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8, true>(p, qh, kh, vh, oh, w, l, st);
+        case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4, true>(p, qh, kh, vh, oh, w, l, st);
+        default: return (int)hipErrorInvalidValue;
+        }
+    }
     switch (p.variant) {
     case kVariantDecode: return launch_partial_cfg<64, 1, 1, 8>(p, qh, kh, vh, oh, w, l, st);
     case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8>(p, qh, kh, vh, oh, w, l, st);
@@ -798,12 +974,20 @@ int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
     const long long rows = (long long)p.B * p.M;
     const long long threads = rows * (p.D / 4);
     const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
-    if (p.D == 128)
-        hipLaunchKernelGGL(gqa_combine_kernel<128>, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
-                           (_Float16 *)o, p.st.o_b, p.st.o_i, p.M, rows, p.splits);
+    hipStream_t st = (hipStream_t)stream;
+    _Float16 *oh = (_Float16 *)o;
+    if (p.D == 128 && p.qknorm)
+        hipLaunchKernelGGL((gqa_combine_kernel<128, true>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
+                           p.st.o_i, p.M, rows, p.splits);
+    else if (p.D == 128)
+        hipLaunchKernelGGL((gqa_combine_kernel<128, false>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
+                           p.st.o_i, p.M, rows, p.splits);
+    else if (p.qknorm)
+        hipLaunchKernelGGL((gqa_combine_kernel<64, true>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
+                           p.st.o_i, p.M, rows, p.splits);
     else
-        hipLaunchKernelGGL(gqa_combine_kernel<64>, grid, dim3(kThreads), 0, (hipStream_t)stream, w, l,
-                           (_Float16 *)o, p.st.o_b, p.st.o_i, p.M, rows, p.splits);
+        hipLaunchKernelGGL((gqa_combine_kernel<64, false>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
+                           p.st.o_i, p.M, rows, p.splits);
     return (int)hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 
 #include "../../include/mga_gqa.h"
 #include "mga_internal.h"
@@ -44,8 +45,9 @@ int rows_for(int variant) {
 // workgroup per compute unit, else 128-row tiles when they cover the chip
 // unsplit, else 64-row tiles (32 for M <= 32) and more key splits, which keep
 // each workgroup's K/V stream short.
-int variant_for(int B, int M, int N, int D) {
+int variant_for(int B, int M, int N, int D, bool qknorm) {
     if (D == 128) return kVariantDecode128;
+    if (qknorm) return M <= 32 ? kVariantDecode : kVariantSmall;  // wave-private rings only
     if (M <= 32) return kVariantDecode;
     const long long two = std::min(2LL, max_splits(N));
     if (M > 128 && (long long)B * ceil_div(M, 256) * two >= kCUs) return kVariantLarge;
@@ -68,7 +70,7 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 
 }  // namespace
 
-int make_plan(int B, int M, int N, int D, int splits, Plan *p) {
+int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     if (B < 0 || M < 0 || N < 1 || splits < 0) return MGA_ERR_INVALID_VALUE;
     if (D != 64 && D != 128) return MGA_ERR_CONFIG;
     const long long nblocks = ceil_div(N, kKeyBlock);
@@ -77,7 +79,9 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p) {
     p->M = M;
     p->N = N;
     p->D = D;
-    p->variant = variant_for(B, M, N, D);
+    p->variant = variant_for(B, M, N, D, qknorm);
+    p->qknorm = qknorm;
+    p->eps = 0.f;
     p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;
@@ -257,6 +261,49 @@ int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *ef
     if (rc != MGA_OK) return rc;
     if (tile_rows) *tile_rows = p.tile_rows;
     if (eff_splits) *eff_splits = p.splits;
+    return MGA_OK;
+}
+
+/* ---- QK-normalised variant ---- */
+
+size_t mga_gqa_qknorm_workspace_bytes(int B, int M, int N, int D, int splits) {
+    mga::Plan p;
+    if (mga::make_plan(B, M, N, D, splits, &p, true) != MGA_OK) return 0;
+    return p.ws_bytes;
+}
+
+int mga_gqa_qknorm_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits) {
+    mga::Plan p;
+    const int rc = mga::make_plan(B, M, N, D, splits, &p, true);
+    if (rc != MGA_OK) return rc;
+    if (tile_rows) *tile_rows = p.tile_rows;
+    if (eff_splits) *eff_splits = p.splits;
+    return MGA_OK;
+}
+
+int mga_gqa_qknorm_check_args(const void *q, const void *k, const void *v, const void *o, int B,
+                              int M, int N, int D, float eps, const int64_t *strides, int splits,
+                              const void *ws, size_t ws_bytes) {
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return MGA_ERR_INVALID_VALUE;
+    mga::Plan p;
+    int rc = mga::make_plan(B, M, N, D, splits, &p, true);
+    if (rc == MGA_OK) rc = mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
+    if (rc != MGA_OK) return rc;
+    return mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
+}
+
+int mga_gqa_qknorm_forward(const void *q, const void *k, const void *v, void *o, int B, int M,
+                           int N, int D, float eps, const int64_t *strides, int splits, void *ws,
+                           size_t ws_bytes, void *stream) {
+    int rc = mga_gqa_qknorm_check_args(q, k, v, o, B, M, N, D, eps, strides, splits, ws, ws_bytes);
+    if (rc != MGA_OK) return rc;
+    if (B == 0 || M == 0) return MGA_OK;
+    mga::Plan p;
+    mga::make_plan(B, M, N, D, splits, &p, true);
+    mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
+    p.eps = eps;
+    if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
+    if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
     return MGA_OK;
 }
 

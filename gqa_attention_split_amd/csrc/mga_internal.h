@@ -18,6 +18,8 @@ struct Strides {
 struct Plan {
     int B, M, N, D;
     bool key_major;   // K stored [N][D] per batch (else [D][N])
+    bool qknorm;      // rms_norm of Q rows and key vectors before the graph
+    float eps;        // rms_norm epsilon (qknorm only)
     Strides st;
     int variant;      // kernel shape, one of the kVariant* values
     int tile_rows;    // query rows per workgroup
@@ -45,8 +47,9 @@ constexpr int max_keys(int D) { return (1 << 30) / D - 1; }
 constexpr int kThreads = 256;
 
 // Fills `p` for a call; returns an mga_status (0 = ok). Host only, no HIP calls.
-// The layout is left contiguous and unchecked; set_layout fixes it.
-int make_plan(int B, int M, int N, int D, int splits, Plan *p);
+// The layout is left contiguous and unchecked; set_layout fixes it. With
+// qknorm the kernel shape comes from the wave-private-ring shapes only.
+int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm = false);
 
 // Checks the nine element strides (q_b, q_i, k_b, k_d, k_n, v_b, v_n, o_b,
 // o_i; NULL = contiguous) against the plan's shape and stores them. Returns

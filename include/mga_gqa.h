@@ -177,6 +177,43 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
 int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits,
                     const void *ws, size_t ws_bytes, void *stream);
 
+/* ---- QK-normalised variant ---------------------------------------------
+ * Attention with QK normalisation (Mirage documentation tutorial "Implement
+ * QK Normalization and Optimize Attention Kernel in Python", the
+ * attention-with-kv-norm page): Q = rms_norm(Q), K = rms_norm(K), then the
+ * same graph. The pages leave rms_norm's axis, eps and weight open; here every
+ * query row and every key vector (a column of head-dim-major K) is divided by
+ * the root mean square of its D entries, eps added inside the root, no weight:
+ *     q-hat = q / sqrt(mean_d q_d^2 + eps),  k-hat likewise per key,
+ *     O = softmax over keys of (q-hat . k-hat) applied to V.
+ * After normalisation |q-hat . k-hat| reaches D, far past fp16 for exp, so
+ * this path keeps a per-row reference maximum and rescales (exact: E / S is
+ * unchanged by a common factor); partials carry log2 of their weight mass.
+ * Numerics: q-hat is rounded to fp16 (with log2(e) folded in) as the graph's
+ * fp16 tensor is; key norms scale the fp32 scores. eps must be finite and
+ * >= 0 (else MGA_ERR_INVALID_VALUE); eps = 0 with an all-zero vector gives
+ * NaN, as the definition does. Same layouts, strides (NULL = contiguous),
+ * status codes and ownership as mga_gqa_forward_strided; the kernel shape is
+ * 32 rows (M <= 32 or D = 128) or 64 rows per workgroup, so the split policy
+ * and workspace size may differ from the plain path's. */
+int mga_gqa_qknorm_forward(const void *q, const void *k, const void *v, void *o,
+                           int B, int M, int N, int D, float eps, const int64_t *strides,
+                           int splits, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes mga_gqa_qknorm_forward needs (same form as
+ * mga_gqa_workspace_bytes, for this path's split count); 0 for invalid
+ * shapes or one split. */
+size_t mga_gqa_qknorm_workspace_bytes(int B, int M, int N, int D, int splits);
+
+/* Tile rows and effective split count of the QK-normalised path (as
+ * mga_gqa_plan). */
+int mga_gqa_qknorm_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
+
+/* Host-only validation of a mga_gqa_qknorm_forward call (no HIP call). */
+int mga_gqa_qknorm_check_args(const void *q, const void *k, const void *v, const void *o,
+                              int B, int M, int N, int D, float eps, const int64_t *strides,
+                              int splits, const void *ws, size_t ws_bytes);
+
 #ifdef __cplusplus
 }
 #endif

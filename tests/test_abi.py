@@ -223,3 +223,35 @@ def test_plan_accepts_any_key_count():
     rc, rows, eff = mga.mga_gqa_plan(2, 256, 1001, 64, 0)
     assert rc == mga.MGA_OK and eff == mga.mga_gqa_effective_splits(2, 256, 1001, 64, 0)
     assert mga.mga_gqa_workspace_bytes(2, 256, 1001, 64, 2) > 0
+
+
+# --------------------------------------------------------- QK norm (host) --
+def test_qknorm_plan_uses_private_ring_shapes():
+    for (B, M, N, D, rows) in [(16, 256, 4096, 64, 64), (128, 256, 16384, 64, 64), (64, 8, 8192, 64, 32),
+                               (64, 1, 4096, 128, 32), (2, 300, 1000, 64, 64)]:
+        rc, r, eff = mga.mga_gqa_qknorm_plan(B, M, N, D, 0)
+        assert rc == mga.MGA_OK and r == rows, (B, M, N, D, r)
+        ws = mga.mga_gqa_qknorm_workspace_bytes(B, M, N, D, 0)
+        if eff == 1:
+            assert ws == 0
+        else:
+            o_bytes = -(-eff * B * M * D * 2 // 256) * 256
+            assert ws == -(-(o_bytes + eff * B * M * 4) // 256) * 256
+
+
+def test_qknorm_check_args():
+    def chk(eps=1e-6, strides=None, **kw):
+        a = dict(B=2, M=256, N=4096, D=64, splits=1)
+        a.update(kw)
+        return mga.mga_gqa_qknorm_check_args(A, A, A, A, a["B"], a["M"], a["N"], a["D"], eps, strides,
+                                             a["splits"], None, 0)
+    assert chk() == mga.MGA_OK
+    assert chk(eps=0.0) == mga.MGA_OK
+    for bad in (-1e-6, float("nan"), float("inf")):
+        assert chk(eps=bad) == mga.MGA_ERR_INVALID_VALUE, bad
+    assert chk(D=96) == mga.MGA_ERR_CONFIG
+    assert chk(N=1001) == mga.MGA_ERR_LAYOUT                          # contiguous K, N % 8 != 0
+    assert chk(N=1001, strides=_st(2, 256, 1001, 64, k_b=1001 * 64, k_d=1, k_n=64)) == mga.MGA_OK
+    assert chk(splits=4) == mga.MGA_ERR_WORKSPACE
+    assert mga.mga_gqa_qknorm_forward(A, A, A, A, 2, 256, 4096, 64, -1.0, None, 1, None, 0,
+                                      None) == mga.MGA_ERR_INVALID_VALUE
