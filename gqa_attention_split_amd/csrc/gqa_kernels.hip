@@ -909,6 +909,24 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     *reinterpret_cast<half4 *>(o + b * o_b + (row - b * M) * o_i + 4 * c) = hv;
 }
 
+// K repack for contiguous head-dim-major K whose rows (N keys) are not
+// 16-byte aligned: each thread writes 8 keys of one row of the copy, rows of
+// ceil8(N) keys, zero past N.
+__global__ __launch_bounds__(256) void repack_k_kernel(const _Float16 *__restrict__ src,
+                                                       _Float16 *__restrict__ dst, long long rows, int N,
+                                                       int n8) {
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per_row = n8 / 8;
+    const long long row = gid / per_row;
+    const int c = (int)(gid - row * per_row) * 8;
+    if (row >= rows) return;
+    const _Float16 *s = src + row * N;
+    half8 out;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = c + j < N ? s[c + j] : (_Float16)0.f;
+    *reinterpret_cast<half8 *>(dst + row * n8 + c) = out;
+}
+
 template <int HD, int QT, int QW, int KS, bool KM, bool QKN>
 int launch_partial_layout(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
                           _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
@@ -965,6 +983,16 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
     case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4>(p, qh, kh, vh, oh, w, l, st);
     default: return (int)hipErrorInvalidValue;
     }
+}
+
+int launch_repack(const Plan &p, const void *k, void *ws, void *stream) {
+    const int n8 = (p.N + 7) & ~7;
+    const long long rows = (long long)p.B * p.D;
+    const long long threads = rows * (n8 / 8);
+    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(repack_k_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, (const _Float16 *)k,
+                       (_Float16 *)((char *)ws + p.repack_off), rows, p.N, n8);
+    return (int)hipGetLastError();
 }
 
 int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {

@@ -82,6 +82,8 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     p->variant = variant_for(B, M, N, D, qknorm);
     p->qknorm = qknorm;
     p->eps = 0.f;
+    p->repack = false;
+    p->repack_off = 0;
     p->tile_rows = rows_for(p->variant);
     p->mtiles = (int)ceil_div(M, p->tile_rows);
     p->nblocks = (int)nblocks;
@@ -113,6 +115,15 @@ int set_layout(Plan *p, const long long *s) {
         v_b = s[5], v_n = s[6], o_b = s[7], o_i = s[8];
     } else {
         q_b = M * D, q_i = D, k_b = D * N, k_d = N, k_n = 1, v_b = N * D, v_n = D, o_b = M * D, o_i = D;
+        if (N % 8 != 0) {
+            // Contiguous K rows start 2-byte aligned only: the partial kernel
+            // reads a copy with rows of ceil8(N) keys from the workspace.
+            const long long n8 = (N + 7) & ~7LL;
+            p->repack = true;
+            p->repack_off = p->ws_bytes;
+            p->ws_bytes += ((size_t)(B * D * n8) * 2 + 255) & ~(size_t)255;
+            k_b = D * n8, k_d = n8;
+        }
     }
     // Row strides up to 2^30 and batch strides up to 2^48 elements keep every
     // product below 2^63; the byte extents are checked against 2^31 below.
@@ -169,8 +180,7 @@ const char *mga_status_string(int status) {
     case MGA_ERR_INVALID_VALUE:
         return "MGA_ERR_INVALID_VALUE: null pointer, negative B/M/splits, or N < 1";
     case MGA_ERR_LAYOUT:
-        return "MGA_ERR_LAYOUT: pointer not 16-byte aligned, or a stride not allowed (contiguous K "
-               "needs N to be a multiple of 8)";
+        return "MGA_ERR_LAYOUT: pointer not 16-byte aligned, or a stride not allowed";
     case MGA_ERR_CONFIG:
         return "MGA_ERR_CONFIG: head dim not 64 or 128, splits above ceil(N/128), N above 2^30/D - 1, "
                "a stride or byte extent too large, or a grid too large";
@@ -195,6 +205,7 @@ int mga_gqa_effective_splits(int B, int M, int N, int D, int splits) {
 size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits) {
     mga::Plan p;
     if (mga::make_plan(B, M, N, D, splits, &p) != MGA_OK) return 0;
+    if (mga::set_layout(&p, nullptr) != MGA_OK) return 0;
     return p.ws_bytes;
 }
 
@@ -222,6 +233,10 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o, int B,
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0) return MGA_OK;
+    if (p.repack) {
+        if (mga::launch_repack(p, k, ws, stream) != 0) return MGA_ERR_HIP;
+        k = (const char *)ws + p.repack_off;
+    }
     return mga::launch_partial(p, q, k, v, o, ws, stream) == 0 ? MGA_OK : MGA_ERR_HIP;
 }
 
@@ -250,6 +265,10 @@ int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
     if (B == 0 || M == 0) return MGA_OK;
+    if (p.repack) {
+        if (mga::launch_repack(p, k, ws, stream) != 0) return MGA_ERR_HIP;
+        k = (const char *)ws + p.repack_off;
+    }
     if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
     if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
     return MGA_OK;
@@ -269,6 +288,7 @@ int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *ef
 size_t mga_gqa_qknorm_workspace_bytes(int B, int M, int N, int D, int splits) {
     mga::Plan p;
     if (mga::make_plan(B, M, N, D, splits, &p, true) != MGA_OK) return 0;
+    if (mga::set_layout(&p, nullptr) != MGA_OK) return 0;
     return p.ws_bytes;
 }
 
@@ -302,6 +322,10 @@ int mga_gqa_qknorm_forward(const void *q, const void *k, const void *v, void *o,
     mga::make_plan(B, M, N, D, splits, &p, true);
     mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
     p.eps = eps;
+    if (p.repack) {
+        if (mga::launch_repack(p, k, ws, stream) != 0) return MGA_ERR_HIP;
+        k = (const char *)ws + p.repack_off;
+    }
     if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
     if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
     return MGA_OK;

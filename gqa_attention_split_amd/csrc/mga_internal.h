@@ -20,6 +20,8 @@ struct Plan {
     bool key_major;   // K stored [N][D] per batch (else [D][N])
     bool qknorm;      // rms_norm of Q rows and key vectors before the graph
     float eps;        // rms_norm epsilon (qknorm only)
+    bool repack;      // contiguous K with N % 8 != 0: copied first to rows of ceil8(N) keys
+    size_t repack_off;  // byte offset of that copy in the workspace
     Strides st;
     int variant;      // kernel shape, one of the kVariant* values
     int tile_rows;    // query rows per workgroup
@@ -53,7 +55,8 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm = fal
 
 // Checks the nine element strides (q_b, q_i, k_b, k_d, k_n, v_b, v_n, o_b,
 // o_i; NULL = contiguous) against the plan's shape and stores them. Returns
-// an mga_status.
+// an mga_status. NULL with N % 8 != 0 plans the K repack (and grows
+// ws_bytes by its size).
 int set_layout(Plan *p, const long long *strides);
 
 // Argument checks shared by every entry point (host only).
@@ -64,5 +67,7 @@ int check_call(const void *q, const void *k, const void *v, const void *o, const
 int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,
                    void *ws, void *stream);
 int launch_combine(const Plan &p, void *o, const void *ws, void *stream);
+// Copies K [B][D][N] into the workspace as [B][D][ceil8(N)] (padding zero).
+int launch_repack(const Plan &p, const void *k, void *ws, void *stream);
 
 }  // namespace mga

@@ -59,7 +59,8 @@ def test_check_args_codes():
     assert _check(M=-1) == mga.MGA_ERR_INVALID_VALUE
     assert _check(N=0) == mga.MGA_ERR_INVALID_VALUE
     assert _check(splits=-1) == mga.MGA_ERR_INVALID_VALUE
-    assert _check(N=4100) == mga.MGA_ERR_LAYOUT
+    assert _check(N=4100) == mga.MGA_OK                     # contiguous K, N % 8 != 0: repacked
+    assert _check(N=4100, splits=1, ws=None, ws_bytes=0) == mga.MGA_ERR_WORKSPACE
     assert _check(k=A + 8) == mga.MGA_ERR_LAYOUT
     assert _check(o=A + 2) == mga.MGA_ERR_LAYOUT
     assert _check(splits=33) == mga.MGA_ERR_CONFIG          # ceil(4096/128) = 32
@@ -95,7 +96,8 @@ def test_check_args_head_dim():
 
 def test_forward_rejects_before_launching():
     # Errors come back before any HIP call, so this runs without a GPU.
-    assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4100, 64, 0, None, 0, None) == mga.MGA_ERR_LAYOUT
+    assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4100, 64, 0, None, 0, None) == mga.MGA_ERR_WORKSPACE
+    assert mga.mga_gqa_forward(A + 2, A, A, A, 2, 256, 4096, 64, 0, None, 0, None) == mga.MGA_ERR_LAYOUT
     assert mga.mga_gqa_forward(A, A, A, A, 2, 256, 4096, 80, 1, None, 0, None) == mga.MGA_ERR_CONFIG
     assert mga.mga_gqa_partial(None, A, A, A, 2, 256, 4096, 128, 1, None, 0, None) == \
         mga.MGA_ERR_INVALID_VALUE
@@ -190,9 +192,10 @@ def test_strided_layouts_accepted():
 
 
 def test_strided_layouts_rejected():
-    # contiguous head-dim-major K needs N % 8 == 0 (rows 16-byte aligned)
+    # explicit head-dim-major strides need rows that start 16-byte aligned;
+    # only the contiguous form (NULL strides) repacks K into the workspace
     assert _check_st(N=1001, k_b=64 * 1001, k_d=1001) == mga.MGA_ERR_LAYOUT
-    assert _check_st(strides=None, N=1001) == mga.MGA_ERR_LAYOUT
+    assert _check_st(strides=None, N=1001) == mga.MGA_ERR_WORKSPACE
     assert _check_st(k_n=2) == mga.MGA_ERR_LAYOUT                      # no unit stride in K
     assert _check_st(k_d=1, k_n=56) == mga.MGA_ERR_LAYOUT              # key rows shorter than D
     assert _check_st(k_d=4088) == mga.MGA_ERR_LAYOUT                   # head-dim rows shorter than N
@@ -250,8 +253,24 @@ def test_qknorm_check_args():
     for bad in (-1e-6, float("nan"), float("inf")):
         assert chk(eps=bad) == mga.MGA_ERR_INVALID_VALUE, bad
     assert chk(D=96) == mga.MGA_ERR_CONFIG
-    assert chk(N=1001) == mga.MGA_ERR_LAYOUT                          # contiguous K, N % 8 != 0
+    assert chk(N=1001) == mga.MGA_ERR_WORKSPACE                       # contiguous K repack needs one
     assert chk(N=1001, strides=_st(2, 256, 1001, 64, k_b=1001 * 64, k_d=1, k_n=64)) == mga.MGA_OK
     assert chk(splits=4) == mga.MGA_ERR_WORKSPACE
     assert mga.mga_gqa_qknorm_forward(A, A, A, A, 2, 256, 4096, 64, -1.0, None, 1, None, 0,
                                       None) == mga.MGA_ERR_INVALID_VALUE
+
+
+def test_repack_workspace_for_unaligned_contiguous_k():
+    """Contiguous K with N % 8 != 0 is copied into the workspace with rows of
+    ceil8(N) keys, after the partials (each part rounded up to 256 bytes)."""
+    for (B, M, N, D) in [(2, 256, 1001, 64), (3, 40, 13, 128), (1, 1, 3, 64), (16, 256, 4095, 64)]:
+        for splits in sorted({1, 0, 2} & set(range(math.ceil(N / mga.KEY_BLOCK) + 1))):
+            eff = mga.mga_gqa_effective_splits(B, M, N, D, splits)
+            part = 0
+            if eff > 1:
+                o_bytes = -(-eff * B * M * D * 2 // 256) * 256
+                part = -(-(o_bytes + eff * B * M * 4) // 256) * 256
+            n8 = -(-N // 8) * 8
+            assert mga.mga_gqa_workspace_bytes(B, M, N, D, splits) == part + -(-B * D * n8 * 2 // 256) * 256
+            assert mga.mga_gqa_check_args(A, A, A, A, B, M, N, D, splits, A,
+                                          mga.mga_gqa_workspace_bytes(B, M, N, D, splits)) == mga.MGA_OK

@@ -162,3 +162,29 @@ def test_kv_shared_by_every_batch(gpu, D):
         o = _run(_t(q, gpu), kx, vx, s)
         assert_parity(o.cpu().numpy(), ref, q, kb, vb, f"shared kv D{D} s{s}")
         assert torch.equal(o, _run(_t(q, gpu), _t(kb, gpu), _t(vb, gpu), s))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", [1, 3, 13, 1001, 4099])
+def test_contiguous_k_with_unaligned_rows_is_repacked(gpu, N, D):
+    """Contiguous K whose rows (N keys) do not start 16-byte aligned: the
+    library copies it into the workspace with rows of ceil8(N) keys. The
+    result equals the padded-row view's bit for bit (same kernel, same
+    operands) and matches the oracle; the QK-normalised path takes the same
+    copy."""
+    import torch
+    B, M = 3, 40
+    q, k, v = make_qkv(B, M, N, seed=1100 + N + D, qk_std=0.3 if D == 64 else 0.25, D=D)
+    tq, tk, tv = _t(q, gpu), _t(k, gpu), _t(v, gpu)
+    ref = oracle.gqa_f64(q, k, v)
+    nblocks = -(-N // mga.KEY_BLOCK)
+    for s in sorted({0, 1, 2, nblocks} & set(range(nblocks + 1))):
+        _say(f"[repack] N={N} D={D} splits={s} workspace={mga.mga_gqa_workspace_bytes(B, M, N, D, s)}")
+        o = _run(tq, tk, tv, s)
+        assert torch.equal(o, _run(tq, _padded_rows(k, gpu, 5), tv, s))
+        assert_parity(o.cpu().numpy(), ref, q, k, v, f"repacked N{N} D{D} s{s}")
+    o = mga.gqa_forward(tq, tk, tv, qk_norm=True)
+    kview = _padded_rows(k, gpu, 11)
+    o2 = mga.gqa_forward(tq, kview, tv, qk_norm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
