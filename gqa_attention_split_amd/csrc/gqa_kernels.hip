@@ -87,7 +87,6 @@ constexpr int K_ROW_BYTES = KT * 2;          // 64: one head dim's 32 keys
 constexpr int LDS_LIMIT = 160 * 1024;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int BUFFER_FLAGS = 0x00020000;     // gfx9 raw buffer descriptor, dword 3
-constexpr uint32_t OOB = 0x80000000u;        // offset past every descriptor's records
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }

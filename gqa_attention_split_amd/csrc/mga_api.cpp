@@ -39,20 +39,28 @@ int rows_for(int variant) {
     }
 }
 
-// Query rows per workgroup. Larger tiles read each K/V tile into fewer
-// workgroups, but need enough (batch, query tile) pairs to cover the chip:
-// 256-row tiles when at most two key splits bring their grid to one
-// workgroup per compute unit, else 128-row tiles when they cover the chip
-// unsplit, else 64-row tiles (32 for M <= 32) and more key splits, which keep
-// each workgroup's K/V stream short.
+// Query rows per workgroup. The rule comes from cold-input tile x split
+// sweeps of the five benchmark shapes on MI355X:
+//   * a tile shape that fills the chip (256 workgroups) without splitting
+//     beats any split configuration: 256 rows, else 128 rows;
+//   * else 256-row tiles if two splits fill the chip;
+//   * else 64-row tiles with key splits, unless even the most splits the key
+//     count allows leave them short of the chip: then 32-row tiles, which
+//     double the workgroups. (At an equal, full workgroup count, 64-row tiles
+//     with twice the splits beat 32-row tiles: half the K/V bytes per
+//     workgroup.)
+// Rows M <= 32 take 32-row tiles. The QK-normalised path has only the
+// wave-private 32- and 64-row shapes.
 int variant_for(int B, int M, int N, int D, bool qknorm) {
     if (D == 128) return kVariantDecode128;
     if (qknorm) return M <= 32 ? kVariantDecode : kVariantSmall;  // wave-private rings only
     if (M <= 32) return kVariantDecode;
-    const long long two = std::min(2LL, max_splits(N));
-    if (M > 128 && (long long)B * ceil_div(M, 256) * two >= kCUs) return kVariantLarge;
-    if (M > 64 && (long long)B * ceil_div(M, 128) >= kCUs) return kVariantMedium;
-    return kVariantSmall;
+    const long long b = B, ms = max_splits(N);
+    if (M > 128 && b * ceil_div(M, 256) >= kCUs) return kVariantLarge;
+    if (M > 64 && b * ceil_div(M, 128) >= kCUs) return kVariantMedium;
+    if (M > 128 && b * ceil_div(M, 256) * std::min(2LL, ms) >= kCUs) return kVariantLarge;
+    if (b * ceil_div(M, 64) * ms >= kCUs) return kVariantSmall;
+    return kVariantDecode;
 }
 
 // Policy: split the keys just enough that the grid reaches one workgroup per

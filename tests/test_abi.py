@@ -139,11 +139,12 @@ def test_split_policy_and_workspace(B, M, N, D):
     (8, 32, 16384, 128, 32, 32),
     (1, 1, 8, 128, 32, 1),
     (256, 64, 1024, 128, 32, 1),
-    (16, 256, 4096, 64, 64, 4),      # few query rows: 64-row tiles, 4 splits fill 256 CUs
-    (2, 256, 4096, 64, 64, 8),       # 32 would fill the chip; chunks keep >= 4 key blocks
+    (16, 256, 4096, 64, 64, 4),      # 64-row tiles, 4 splits fill 256 CUs
+    (2, 256, 4096, 64, 32, 8),       # 64-row tiles would reach 64 workgroups at most: 32-row tiles
     (2, 256, 32768, 64, 64, 32),
     (64, 8, 8192, 64, 32, 4),        # decode-like rows: 32-row tiles
-    (128, 256, 16384, 64, 256, 2),   # 256-row tiles fill the chip with two splits
+    (128, 256, 16384, 64, 128, 1),   # 128-row tiles fill the chip unsplit
+    (70, 300, 16384, 64, 256, 2),    # 256-row tiles fill the chip with two splits (128-row do not unsplit)
     (128, 130, 520, 64, 128, 1),     # 128-row tiles fill the chip unsplit
     (1024, 256, 1024, 64, 256, 1),   # 256-row tiles already fill the chip
 ])
@@ -212,8 +213,10 @@ def test_strided_layouts_rejected():
     assert _check_st(k_d=1, k_n=1 << 18, k_b=0) == mga.MGA_OK          # (4095 * 2^18 + 64) * 2 < 2^31
     assert _check_st(k_d=1, k_n=1 << 19, k_b=0) == mga.MGA_ERR_CONFIG
     assert _check_st(v_n=1 << 19) == mga.MGA_ERR_CONFIG
-    assert _check_st(q_i=1 << 25) == mga.MGA_ERR_CONFIG                # 63 rows * 2^26 bytes (64-row tiles)
-    assert _check_st(q_i=1 << 24) == mga.MGA_OK                        # (63 * 2^24 + 64) * 2 < 2^31
+    rows = mga.mga_gqa_plan(2, 256, 4096, 64, 1)[1]                  # a workgroup's Q rows
+    q_bad = next(1 << e for e in range(3, 31) if ((rows - 1) * (1 << e) + 64) * 2 >= 1 << 31)
+    assert _check_st(q_i=q_bad) == mga.MGA_ERR_CONFIG
+    assert _check_st(q_i=q_bad // 2) == mga.MGA_OK
     assert _check_st(o_i=(1 << 30) + 8) == mga.MGA_ERR_CONFIG
     assert _check_st(q_b=(1 << 48) + 8) == mga.MGA_ERR_CONFIG
     # a layout error comes back from the strided forward without launching
