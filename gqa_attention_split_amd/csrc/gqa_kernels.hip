@@ -523,15 +523,19 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     };
 
     // Q for the workgroup's rows -> LDS rows of HD*2 bytes (rows past M read
-    // zero). Issued before any K/V tile so that the first step finds it.
+    // zero). Issued before any K/V tile so that the first step finds it. The
+    // 16-byte units of row r are XORed with r & 7: the operand reads take one
+    // unit of 32 consecutive rows, which then fall in distinct banks.
     {
         constexpr int QLPR = HD / 8, QRPI = 64 / QLPR;  // lanes per row, rows per instruction
         const int qrows = min(C::ROWS, M - qrow0);
         const i32x4 qr = make_rsrc(q + b * st.q_b + (size_t)qrow0 * st.q_i,
                                    ((uint32_t)(qrows - 1) * (uint32_t)st.q_i + HD) * 2);
-        const uint32_t lrow = lane / QLPR, lcol = 16 * (lane % QLPR);
-        for (int j = wave; j < C::Q_OPS; j += C::NWAVES)
-            dma16(qr, (j * QRPI + lrow) * (uint32_t)st.q_i * 2 + lcol, lds0 + C::Q_OFF + j * 1024);
+        const uint32_t lrow = lane / QLPR, lunit = lane % QLPR;
+        for (int j = wave; j < C::Q_OPS; j += C::NWAVES) {
+            const uint32_t row = j * QRPI + lrow;
+            dma16(qr, row * (uint32_t)st.q_i * 2 + 16 * (lunit ^ (row & 7)), lds0 + C::Q_OFF + j * 1024);
+        }
     }
 
     float16v oacc[DT][QT];
@@ -557,10 +561,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     auto load_q = [&]() {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-            const char *row = smem + C::Q_OFF + (qbase - qrow0 + 32 * qt + (lane & 31)) * G::Q_ROW_BYTES + 16 * h;
+            const int r = qbase - qrow0 + 32 * qt + (lane & 31);  // staging row
+            const char *row = smem + C::Q_OFF + r * G::Q_ROW_BYTES;
             half8 x[KSTEPS];
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) x[kk] = *reinterpret_cast<const half8 *>(row + 32 * kk);
+            for (int kk = 0; kk < KSTEPS; ++kk)  // head dims 16kk + 8h ..: unit 2kk + h, swizzled
+                x[kk] = *reinterpret_cast<const half8 *>(row + 16 * ((2 * kk + h) ^ (r & 7)));
             if constexpr (QKN) {
                 float ss = 0.f;
 #pragma unroll
