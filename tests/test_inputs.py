@@ -42,3 +42,16 @@ def test_work_and_bytes_formulas():
     cfg = CONFIGS["gqa_b16_m256_n4096"]
     assert cfg.flops == 4 * 16 * 256 * 4096 * 64
     assert cfg.algorithmic_bytes == 256 * 16 * (256 + 4096)
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_scores_stay_far_below_fp16_exp_overflow(name):
+    """The graph has no max subtraction: exp(a) must fit fp16 (a < ln 65504 ~
+    11.09). Every workload's largest |score| (all rows for the small ones,
+    sampled batches and rows for the large) stays below 6."""
+    cfg = CONFIGS[name]
+    q, k, _ = make_config(cfg)
+    bs = np.arange(cfg.B) if cfg.B * cfg.M * cfg.N <= 1 << 23 else np.linspace(0, cfg.B - 1, 4).astype(int)
+    rows = np.arange(cfg.M) if cfg.M <= 16 else np.linspace(0, cfg.M - 1, 16).astype(int)
+    a = np.matmul(q[bs][:, rows].astype(np.float64), k[bs].astype(np.float64))
+    assert float(np.max(np.abs(a))) < 6.0, float(np.max(np.abs(a)))
