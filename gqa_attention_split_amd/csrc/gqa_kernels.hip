@@ -275,14 +275,18 @@ __device__ __forceinline__ void issue_tile(const _Float16 *kp, uint32_t krec, co
     for (int x = 0; x < PER; ++x) dma16(vr, t.voff[x], lds + Geo<HD>::V_PART + (qw * PER + x) * 1024);
 }
 
-// Returns the LDS byte offset x (< 2^18) unchanged, but the compiler must
-// assume it changed: used on a per-lane LDS base inside the loop so that it
-// is not hoisted as base + each read's constant (one register and one add per
-// read per step). The mask shows the value is non-negative, which lets each
-// read's constant go into the instruction's offset field.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x & 0x3ffff;
+// Returns p, a pointer into the kernel's LDS block (byte offset below 2^18),
+// but the compiler must assume it changed: the per-lane base of a tile's
+// operand reads (tile offset + lane offset) is formed once per step, and each
+// read's constant goes into the instruction's unsigned offset field. Left to
+// itself the compiler folds the tile offset and one read's constant into a
+// scalar base, which leaves the other reads' constants negative: one add per
+// read.
+__device__ __forceinline__ const char *lds_base(const char *smem, const char *p) {
+    uint32_t off = (uint32_t)(p - smem);
+    asm volatile("" : "+v"(off));
+    __builtin_assume(off < (1u << 18));
+    return smem + off;
 }
 
 // Per-lane LDS byte offsets (within a tile) of the transposed operand reads.
@@ -641,9 +645,9 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     };
     auto load_k = [&](const char *tile, half8 (&a)[KSTEPS]) {
         if constexpr (KM)
-            read_k_km<HD>(tile, opaque(lo.krow), lo.kx, a);
+            read_k_km<HD>(lds_base(smem, tile + lo.krow), 0, lo.kx, a);
         else
-            read_k<HD>(tile + opaque(lo.k), a);
+            read_k<HD>(lds_base(smem, tile + lo.k), a);
     };
 
     if constexpr (C::PRIVATE) {
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             half8 a[2][DT];
             const char *vbase[DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vbase[dt] = tile_at(it) + opaque(lo.v[dt]);
+            for (int dt = 0; dt < DT; ++dt) vbase[dt] = lds_base(smem, tile_at(it) + lo.v[dt]);
             read_v<HD>(vbase, a);
             pv<HD, QT>(a, p, oacc);
         };
