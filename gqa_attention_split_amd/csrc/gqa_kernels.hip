@@ -745,15 +745,32 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         g1(1, s1);
         sm_last(s0, 0);         // tile 0 is the last one when niter == 1
         int it = 2;
+        // Phases of a step: the second product of tile it-2 (MFMA), then the
+        // first product of tile it (MFMA) and the softmax of tile it-1 (VALU).
+        // The barrier each step starts both waves of a SIMD in the same phase;
+        // the second wave on each SIMD (waves NWAVES/2 ..) takes the softmax
+        // before the first product, so that one wave of the pair issues MFMAs
+        // while the other issues VALU. The scheduling barriers keep the
+        // compiler from merging the phases back.
+        const bool late = wave >= C::NWAVES / 2;
+        auto body = [&](int i, float16v (&sa)[QT], float16v (&sb)[QT]) {
+            g2(i - 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (late) {
+                sm(sb);
+                __builtin_amdgcn_sched_barrier(0);
+                g1(i, sa);
+            } else {
+                g1(i, sa);
+                __builtin_amdgcn_sched_barrier(0);
+                sm(sb);
+            }
+        };
         for (; it + 1 < niter; it += 2) {
             sync();
-            g2(it - 2);
-            g1(it, s0);
-            sm(s1);             // tile it-1
+            body(it, s0, s1);   // softmax of tile it-1
             sync();
-            g2(it - 1);
-            g1(it + 1, s1);
-            sm(s0);             // tile it
+            body(it + 1, s1, s0);
         }
         if (it < niter) {       // one more full step, it even
             sync();
