@@ -31,9 +31,10 @@
  * instead (see there), including K stored key-major.
  * The head dimension D is 64 (the tutorial graph) or 128 (the tutorial's
  * launch example: Q (64, 1, 128), K (64, 128, 4096), V (64, 4096, 128)).
- * Pointers must be 16-byte aligned; for contiguous K, N must be a multiple
- * of 8 (every K row then starts on a 16-byte boundary). N is at most
- * 2^30 / D - 1.
+ * Pointers must be 16-byte aligned. N is at most 2^30 / D - 1 and need not
+ * be a multiple of anything: contiguous K whose rows (N keys) do not start
+ * on 16-byte boundaries (N % 8 != 0) is first copied by the library into the
+ * workspace with rows of ceil8(N) keys (one extra pass over K).
  *
  * Numerics: fp16 MFMA products with fp32 accumulation; E = exp(A) in fp32
  * via the hardware exp2 of log2(e) Q rounded to fp16; P = fp16(E), rounded to
@@ -101,17 +102,23 @@ int mga_gqa_choose_splits(int B, int M, int N, int D);
  * arguments mga_gqa_check_args would reject with INVALID_VALUE or CONFIG. */
 int mga_gqa_effective_splits(int B, int M, int N, int D, int splits);
 
-/* Bytes of workspace mga_gqa_forward needs: 0 when the effective split count
- * s is 1; else the normalised partials o[s][B][M][D] in fp16 (s*B*M*D*2
- * bytes, rounded up to 256) followed by the denominators L[s][B][M] in fp32
- * (s*B*M*4 bytes), the total rounded up to 256. Its contents need no
- * initialisation. Returns 0 for invalid shapes. */
+/* Bytes of workspace mga_gqa_forward needs: with an effective split count
+ * s > 1, the normalised partials o[s][B][M][D] in fp16 (s*B*M*D*2 bytes,
+ * rounded up to 256) followed by the denominators L[s][B][M] in fp32
+ * (s*B*M*4 bytes), rounded up to 256; then, when N % 8 != 0, the copy of K
+ * with rows of ceil8(N) keys (B*D*ceil8(N)*2 bytes, rounded up to 256). 0
+ * when neither applies. Its contents need no initialisation. Returns 0 for
+ * invalid shapes. Enough for mga_gqa_forward_strided too (which never copies
+ * K). */
 size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
 
 /* The launch geometry the library picks (host only): query rows per
- * workgroup (D = 64: 32, 64, 128 or 256 -- the largest tile whose workgroups
- * still cover all 256 compute units without splitting, else 64, or 32 for
- * M <= 32; D = 128: 32) and the effective split count. Either output pointer
+ * workgroup and the effective split count. D = 64: 256 or 128 rows when that
+ * tile alone gives at least 256 workgroups (one per compute unit), else 256
+ * rows when two splits do, else 64 rows, or 32 rows when even the most splits
+ * leave 64-row tiles short of 256 workgroups (and always for M <= 32);
+ * D = 128: 32 rows. Splits then bring the grid to 256 workgroups, each
+ * keeping at least 4 blocks of 128 keys. Either output pointer
  * may be NULL. Returns MGA_OK, INVALID_VALUE or CONFIG for the shape; the
  * memory layout is not part of the plan. */
 int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
@@ -161,10 +168,11 @@ int mga_gqa_check_args_strided(const void *q, const void *k, const void *v, cons
                                int B, int M, int N, int D, const int64_t *strides, int splits,
                                const void *ws, size_t ws_bytes);
 
-/* Only the split-KV partial kernel (the for-loop over keys). With one
- * effective split it writes O directly (normalised, fp16); otherwise it
- * writes the normalised partials and denominators into `ws` and leaves `o`
- * untouched. Same arguments and checks as mga_gqa_forward. */
+/* Only the split-KV partial kernel (the for-loop over keys; preceded by the
+ * K copy when N % 8 != 0). With one effective split it writes O directly
+ * (normalised, fp16); otherwise it writes the normalised partials and
+ * denominators into `ws` and leaves `o` untouched. Same arguments and checks
+ * as mga_gqa_forward. */
 int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
                     int B, int M, int N, int D, int splits, void *ws, size_t ws_bytes,
                     void *stream);
