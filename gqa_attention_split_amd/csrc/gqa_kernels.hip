@@ -1006,6 +1006,7 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
     case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8>(p, qh, kh, vh, oh, w, l, st);
     case kVariantMedium: return launch_partial_cfg<64, 2, 2, 4>(p, qh, kh, vh, oh, w, l, st);
     case kVariantLarge: return launch_partial_cfg<64, 2, 4, 2>(p, qh, kh, vh, oh, w, l, st);
+    case kVariantSmallShared: return launch_partial_cfg<64, 1, 2, 4>(p, qh, kh, vh, oh, w, l, st);
     case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4>(p, qh, kh, vh, oh, w, l, st);
     default: return (int)hipErrorInvalidValue;
     }

@@ -33,7 +33,8 @@ int rows_for(int variant) {
     switch (variant) {
     case kVariantDecode:
     case kVariantDecode128: return 32;
-    case kVariantSmall: return 64;
+    case kVariantSmall:
+    case kVariantSmallShared: return 64;
     case kVariantMedium: return 128;
     default: return 256;
     }
@@ -101,6 +102,12 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);
+    // 64-row tiles over split key ranges run on the shared ring (plain path
+    // only: QK normalisation keeps wave-private rings). With a short key
+    // stream per workgroup its smaller end-of-kernel reduction wins (cold
+    // A/B: 7% at (16, 256, 4096) x 4 splits and (2, 256, 32768) x 32); an
+    // unsplit stream keeps the private ring (2% faster at (64, 256, 4096)).
+    if (!qknorm && p->variant == kVariantSmall && p->splits > 1) p->variant = kVariantSmallShared;
     if (N > max_keys(D)) return MGA_ERR_CONFIG;
     const long long groups = ceil_div((long long)B * p->splits, 8) * 8 * p->mtiles;
     if (groups > INT_MAX || (long long)B * M > INT_MAX / D) return MGA_ERR_CONFIG;

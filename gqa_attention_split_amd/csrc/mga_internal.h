@@ -41,6 +41,10 @@ constexpr int kVariantLarge = 3;   // (2, 4, 2), 256 rows per workgroup, shared 
 // Head dim 128: (1, 1, 4), 32 rows per workgroup, 4 waves with wave-private
 // rings of two 16 KiB tiles.
 constexpr int kVariantDecode128 = 4;
+// (1, 2, 4): 64 rows per workgroup on a shared ring, for split key ranges:
+// its cross-stream reduction sums 4 streams of 32-row partials, not 8 of
+// 64-row ones.
+constexpr int kVariantSmallShared = 5;
 
 constexpr int kKeyBlock = 128;
 // Buffer descriptors address one batch's K or V with 32-bit byte offsets:

@@ -239,16 +239,16 @@ def test_partial_then_combine_matches_forward(gpu, D):
         assert torch.equal(o, o_fwd)
 
 
-@pytest.mark.parametrize("B,M,N,D", [(16, 256, 4096, 64), (64, 8, 8192, 64), (3, 100, 1000, 64),
+@pytest.mark.parametrize("B,M,N,D", [(16, 256, 4096, 64), (64, 200, 520, 64), (64, 8, 8192, 64), (3, 100, 1000, 64),
                                      (128, 130, 520, 64), (128, 130, 264, 64),   # 128-row tiles: refilled / resident ring
                                      (256, 257, 520, 64), (256, 260, 136, 64),   # 256-row tiles: refilled / resident ring
                                      (64, 1, 4096, 128), (3, 33, 1000, 128)])    # head dim 128: 32-row tiles
 def test_partial_then_combine_each_tile_shape(gpu, B, M, N, D):
     """Every query-tile shape the plan can pick (32, 64, 128 and 256 rows at
-    head dim 64, wave-private and shared rings, the shared ring both refilled
-    and with the whole chunk resident; 32 rows at head dim 128): partial +
-    combine equals forward bit for bit, and a reused workspace gives the same
-    bits on every call."""
+    head dim 64; 64 rows on the wave-private ring unsplit and on the shared
+    ring when split; the shared ring both refilled and with the whole chunk
+    resident; 32 rows at head dim 128): partial + combine equals forward bit
+    for bit, and a reused workspace gives the same bits on every call."""
     import torch
     q, k, v = make_qkv(B, M, N, seed=31, qk_std=0.3 if D == 64 else 0.25, D=D)
     tq, tk, tv = (to_dev(x, gpu) for x in (q, k, v))
