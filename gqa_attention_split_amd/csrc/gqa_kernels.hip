@@ -150,9 +150,10 @@ struct Cfg {
     static constexpr int PER = G::DMA / QW;     // K (and V) DMA instructions per wave per tile
     static constexpr int TILE_OPS = 2 * PER;    // DMA instructions per wave per tile
     static constexpr bool PRIVATE = QW == 1;
-    // Shared ring: each buffer holds one tile per stream; step `it` refills
-    // the buffer of tile it-3 (QT = 1: three-stage pipeline) or it-2 (QT > 1:
-    // two-stage), so DIST = STAGES - 3 or STAGES - 2 tiles are in flight.
+    // Shared ring: each buffer holds one tile per stream. Every wave is done
+    // with tile it-2 after step it-1, so step `it` may refill its buffer
+    // (DIST = STAGES - 2 tiles in flight); QT = 1 refills tile it-3's buffer
+    // instead (STAGES - 3 in flight), which timed faster for that shape.
     static constexpr int STAGE_BYTES = KS * TILE_BYTES;
     static constexpr int STAGES = PRIVATE ? 2 : cmin(LDS_LIMIT / STAGE_BYTES, 10);
     static constexpr int DIST = PRIVATE ? 2 : QT == 1 ? STAGES - 3 : STAGES - 2;
@@ -718,84 +719,67 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         // Two schedules, chosen by the tile shape from cold A/B timings
         // (QT = 1: 64 rows on two query waves; QT = 2: 128 and 256 rows).
         if constexpr (QT == 1) {
-            // Step `it` runs the first product of tile it, the softmax numerators
-            // of tile it-1 and the second product of tile it-2. The three are
-            // independent, so each wave's instruction stream always holds both
-            // MFMA and VALU work. The second product runs first in a step, so the
-            // softmax of the same step may overwrite the weights p it consumed;
-            // the scores alternate between s0 and s1.
-            float16v s0[QT], s1[QT];
+            // Two-stage pipeline with a phase offset. Step `it` runs the first
+            // product of tile it, the second product of tile it-1 and one
+            // softmax: of tile it in an early wave (after the products), of
+            // tile it-1 in a late wave (before them). The two waves of a SIMD
+            // are one early (w < NWAVES/2) and one late (w + NWAVES/2): the
+            // barrier of each step starts both together, and then one issues
+            // MFMAs while the other issues VALU.
+            float16v s[QT];
             half8 p[QT][2];
-            auto g1 = [&](int it, float16v (&sv)[QT]) {
+            auto g1 = [&](int it) {
                 half8 a[KSTEPS];
                 load_k(tile_at(it), a);
-                scores<HD, QT>(a, qf, sv);
+                scores<HD, QT>(a, qf, s);
             };
             // Tiles before a stream's last (it <= niter - 2) lie inside the chunk.
-            auto sm = [&](const float16v (&sv)[QT]) { softmax<QT, false>(sv, p, lsum, 0); };
-            auto sm_last = [&](const float16v (&sv)[QT], int it) { softmax_last(it, sv, p); };
+            auto sm = [&]() { softmax<QT, false>(s, p, lsum, 0); };
             auto g2 = [&](int it) {
                 half8 a[2][DT];
                 const char *vbase[DT];
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < DT; ++dt) vbase[dt] = lds_base(smem, tile_at(it) + lo.v[dt]);
                 read_v<HD>(vbase, a);
                 pv<HD, QT>(a, p, oacc);
             };
             const int niter = ntiles;
-            sync();                 // step 0
-            g1(0, s0);
-            sync();                 // step 1 (tile 1 may lie past the chunk: zeros, unused)
-            g1(1, s1);
-            sm_last(s0, 0);         // tile 0 is the last one when niter == 1
-            int it = 2;
-            // Phases of a step: the second product of tile it-2 (MFMA), then the
-            // first product of tile it (MFMA) and the softmax of tile it-1 (VALU).
-            // The barrier each step starts both waves of a SIMD in the same phase;
-            // the second wave on each SIMD (waves NWAVES/2 ..) takes the softmax
-            // before the first product, so that one wave of the pair issues MFMAs
-            // while the other issues VALU. The scheduling barriers keep the
-            // compiler from merging the phases back.
-            const bool late = wave >= C::NWAVES / 2;
-            auto body = [&](int i, float16v (&sa)[QT], float16v (&sb)[QT]) {
-                g2(i - 2);
-                __builtin_amdgcn_sched_barrier(0);
-                if (late) {
-                    sm(sb);
+            // The scheduling barriers keep the compiler from merging the
+            // phases. The orders run in separate loops, so that neither one's
+            // live values burden the other's registers.
+            if (wave >= C::NWAVES / 2) {  // late
+                sync();                   // step 0
+                g1(0);
+                for (int it = 1; it < niter; ++it) {
+                    sync();
+                    sm();                 // tile it-1
                     __builtin_amdgcn_sched_barrier(0);
-                    g1(i, sa);
-                } else {
-                    g1(i, sa);
+                    g1(it);
+                    g2(it - 1);
                     __builtin_amdgcn_sched_barrier(0);
-                    sm(sb);
                 }
-            };
-            for (; it + 1 < niter; it += 2) {
-                sync();
-                body(it, s0, s1);   // softmax of tile it-1
-                sync();
-                body(it + 1, s1, s0);
+            } else {                      // early
+                sync();                   // step 0
+                g1(0);
+                int it = 1;
+                if (niter > 1) {
+                    sm();
+                    for (; it + 1 < niter; ++it) {
+                        sync();
+                        g1(it);
+                        g2(it - 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        sm();             // tile it
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    sync();               // step niter-1: the last tile's softmax may be masked
+                    g1(it);
+                    g2(it - 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            if (it < niter) {       // one more full step, it even
-                sync();
-                g2(it - 2);
-                g1(it, s0);
-                sm(s1);             // tile it-1
-                ++it;
-            }
-            // Drain: tiles niter-2 and niter-1 still need their second product,
-            // tile niter-1 its softmax (niter == 1: only tile 0's product).
-            if (niter == 1) {
-                g2(0);
-            } else if (it & 1) {    // last step even: tile niter-1's scores in s0
-                g2(niter - 2);
-                sm_last(s0, niter - 1);
-                g2(niter - 1);
-            } else {                // last step odd: tile niter-1's scores in s1
-                g2(niter - 2);
-                sm_last(s1, niter - 1);
-                g2(niter - 1);
-            }
+            softmax_last(niter - 1, s, p);
+            g2(niter - 1);
         } else {
             // Two-stage pipeline, the same order in every wave. Step `it`
             // reads tile it's K operand, runs the second product of tile it-1
