@@ -47,7 +47,7 @@ def parse_args():
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--graph-steps", type=int, default=200, help="steps captured per HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=1.5,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle baseline sample (the whole workload "
                          "is repeated until it is reached)")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",

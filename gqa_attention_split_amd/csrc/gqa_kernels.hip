@@ -945,6 +945,10 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
 // O = fp16(sum_s L_s o_s / sum_s L_s), both sums in split order.
 // With LSE (QK normalisation) the workspace holds lse_s = log2 of each
 // split's weight mass; the weights are then 2^(lse_s - max_s lse_s).
+// The partials sit in L2 or the Infinity Cache and each thread is bound by
+// their latency. Up to four splits, a thread issues every load before it sums
+// any; more splits go through an 8-way unrolled loop (each form measured the
+// faster one in its range on MI355X). Both sum in split order.
 template <int HD, bool LSE>
 __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__restrict__ ws_o,
                                                           const float *__restrict__ ws_l,
@@ -959,15 +963,40 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     [[maybe_unused]] float lmax = -__builtin_inff();
     if constexpr (LSE)
         for (int s = 0; s < nsplit; ++s) lmax = __builtin_fmaxf(lmax, ws_l[(long long)s * rows + row]);
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) {
-        const long long prow = (long long)s * rows + row;
-        float ls = ws_l[prow];
-        if constexpr (LSE) ls = ls > -__builtin_inff() ? __builtin_amdgcn_exp2f(ls - lmax) : 0.f;
-        const half4 os = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
-        l += ls;
+    auto weight = [&](float ls) {
+        if constexpr (LSE) return ls > -__builtin_inff() ? __builtin_amdgcn_exp2f(ls - lmax) : 0.f;
+        return ls;
+    };
+    if (nsplit <= 4) {
+        float ls[4];
+        half4 os[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += ls * (float)os[i];
+        for (int s = 0; s < 4; ++s) {
+            if (s < nsplit) {
+                const long long prow = (long long)s * rows + row;
+                ls[s] = ws_l[prow];
+                os[s] = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < nsplit) {
+                const float w = weight(ls[s]);
+                l += w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += w * (float)os[s][i];
+            }
+        }
+    } else {
+#pragma unroll 8
+        for (int s = 0; s < nsplit; ++s) {
+            const long long prow = (long long)s * rows + row;
+            const float w = weight(ws_l[prow]);
+            const half4 os = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
+            l += w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += w * (float)os[i];
+        }
     }
     half4 hv;
 #pragma unroll
