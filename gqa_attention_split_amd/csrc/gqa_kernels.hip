@@ -754,6 +754,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 pv<HD, QT>(a, p, oacc);
             };
             const int niter = ntiles;
+            // Step it needs the K part of tile it and the V part of tile
+            // it-1, which was issued before it: the step's wait leaves the
+            // V part of tile it in flight (each wave issues a tile's K
+            // instructions before its V instructions; they complete in
+            // order, and the barrier makes every wave's share visible).
+            auto sync = [&]() { sync_tile<(DIST - 1) * C::TILE_OPS + C::PER>(); };
             // The scheduling barriers keep the compiler from merging the
             // phases. The orders run in separate loops, so that neither one's
             // live values burden the other's registers.
@@ -794,6 +800,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 }
             }
             softmax_last(niter - 1, s, p);
+            sync_tile<DIST * C::TILE_OPS>();  // the V part of the last tile landed for every wave
             g2(niter - 1);
         } else {
             // Two-stage pipeline, the same order in every wave. Step `it`
