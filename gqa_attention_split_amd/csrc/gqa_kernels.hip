@@ -39,8 +39,9 @@
 //     any of its MFMAs run.
 //   * shared (QW > 1): the QW waves of a stream share each tile; a ring of
 //     STAGES tiles per stream, one workgroup barrier per step, and a
-//     three-phase software pipeline (first product of tile it, softmax of
-//     it-1, second product of it-2).
+//     two-stage software pipeline: step it runs the first product of tile it
+//     and the second product of tile it-1, with the softmax of one of them
+//     (64-row tiles: the two waves of each SIMD take opposite phases).
 // After the loop the KS streams of a query group are summed in LDS in a fixed
 // order; with one split the kernel writes O = fp16(W / L), otherwise the
 // normalised partial o_s = fp16(W / L) and L go to the caller's workspace for
@@ -153,7 +154,8 @@ struct Cfg {
     // Shared ring: each buffer holds one tile per stream. Every wave is done
     // with tile it-2 after step it-1, so step `it` may refill its buffer
     // (DIST = STAGES - 2 tiles in flight); QT = 1 refills tile it-3's buffer
-    // instead (STAGES - 3 in flight), which timed faster for that shape.
+    // instead (STAGES - 3 in flight), which timed faster for that shape (one
+    // tile more or fewer in flight was slower, measured cold on MI355X).
     static constexpr int STAGE_BYTES = KS * TILE_BYTES;
     static constexpr int STAGES = PRIVATE ? 2 : cmin(LDS_LIMIT / STAGE_BYTES, 10);
     static constexpr int DIST = PRIVATE ? 2 : QT == 1 ? STAGES - 3 : STAGES - 2;
