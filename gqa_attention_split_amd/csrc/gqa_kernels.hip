@@ -156,9 +156,12 @@ struct Cfg {
     // (DIST = STAGES - 2 tiles in flight); QT = 1 refills tile it-3's buffer
     // instead (STAGES - 3 in flight), which timed faster for that shape (one
     // tile more or fewer in flight was slower, measured cold on MI355X).
+    // With QK normalisation the ring leaves room for the key-scale slots
+    // (one stage fewer) and refills tile it-2's buffer.
     static constexpr int STAGE_BYTES = KS * TILE_BYTES;
-    static constexpr int STAGES = PRIVATE ? 2 : cmin(LDS_LIMIT / STAGE_BYTES, 10);
-    static constexpr int DIST = PRIVATE ? 2 : QT == 1 ? STAGES - 3 : STAGES - 2;
+    static constexpr int SCR_BYTES = QKN ? NWAVES * 128 : 0;
+    static constexpr int STAGES = PRIVATE ? 2 : cmin((LDS_LIMIT - SCR_BYTES) / STAGE_BYTES, 10);
+    static constexpr int DIST = PRIVATE ? 2 : QT == 1 && !QKN ? STAGES - 3 : STAGES - 2;
     static constexpr int RING_BYTES = PRIVATE ? NWAVES * 2 * TILE_BYTES : STAGES * STAGE_BYTES;
     // Q staging: past the private rings, or in shared-ring buffers that the
     // prologue leaves empty (DIST .. STAGES-1).
@@ -168,14 +171,14 @@ struct Cfg {
     // One wave's epilogue region: its W rows (fp32), L per row, and with QK
     // normalisation the running maximum per row.
     static constexpr int RED_BYTES = 32 * QT * G::RED_ROW_BYTES + 32 * QT * 4 * (QKN ? 2 : 1);
-    // QK normalisation: 128 bytes per wave to move key scales between lanes.
-    static constexpr int SCR_BYTES = QKN ? NWAVES * 128 : 0;
+    // QK normalisation: 128 bytes per wave (SCR_BYTES) to move key scales
+    // between lanes.
     static constexpr int SCR_OFF = cmax(cmax(RING_BYTES, Q_OFF + Q_BYTES), NWAVES * RED_BYTES);
     static constexpr int LDS_BYTES = SCR_OFF + SCR_BYTES;
-    static_assert(!QKN || PRIVATE, "QK normalisation runs on the wave-private ring");
+    static_assert(!QKN || PRIVATE || QT == 1, "QK normalisation: wave-private ring or 32-row query waves");
     static constexpr int DW = HD / KS;                // head dims each wave finalises
     static constexpr int VPL = 32 * QT * DW / 64;     // values per lane in the final write
-    static_assert(PRIVATE || STAGES >= 5, "shared ring depth");
+    static_assert(PRIVATE || STAGES >= (QKN ? 4 : 5), "shared ring depth");
     static_assert(PRIVATE || Q_OFF + Q_BYTES <= RING_BYTES, "Q staging inside the free ring buffers");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS budget");
     static_assert(DIST * TILE_OPS < 64, "vmcnt range");
@@ -647,6 +650,14 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         else
             softmax<QT, true>(sv, pv_, lsum, lim - 4 * h);
     };
+    [[maybe_unused]] auto softmax_last_qkn = [&](int it, const float16v (&sv)[QT], const float16v &rkv,
+                                                 half8 (&pv_)[QT][2]) {
+        const int lim = len - tile_key(it);
+        if (lim >= KT)
+            softmax_qkn<DT, QT, false>(sv, rkv, rq, pv_, lsum, m_run, real, oacc, 0);
+        else
+            softmax_qkn<DT, QT, true>(sv, rkv, rq, pv_, lsum, m_run, real, oacc, lim - 4 * h);
+    };
     auto load_k = [&](const char *tile, half8 (&a)[KSTEPS]) {
         if constexpr (KM)
             read_k_km<HD>(lds_base(smem, tile + lo.krow), 0, lo.kx, a);
@@ -740,13 +751,23 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             // MFMAs while the other issues VALU.
             float16v s[QT];
             half8 p[QT][2];
+            [[maybe_unused]] float16v rk;  // QK normalisation: the key scales of the tile in s
             auto g1 = [&](int it) {
                 half8 a[KSTEPS];
                 load_k(tile_at(it), a);
                 scores<HD, QT>(a, qf, s);
+                if constexpr (QKN) key_scales(a, rk);
             };
             // Tiles before a stream's last (it <= niter - 2) lie inside the chunk.
-            auto sm = [&]() { softmax<QT, false>(s, p, lsum, 0); };
+            // With QK normalisation the softmax may rescale W and L: in either
+            // phase order it runs before the tile's own second product, so
+            // W and L then hold only tiles already relative to the old maximum.
+            auto sm = [&]() {
+                if constexpr (QKN)
+                    softmax_qkn<DT, QT, false>(s, rk, rq, p, lsum, m_run, real, oacc, 0);
+                else
+                    softmax<QT, false>(s, p, lsum, 0);
+            };
             auto g2 = [&](int it) {
                 half8 a[2][DT];
                 const char *vbase[DT];
@@ -801,7 +822,10 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            softmax_last(niter - 1, s, p);
+            if constexpr (QKN)
+                softmax_last_qkn(niter - 1, s, rk, p);
+            else
+                softmax_last(niter - 1, s, p);
             sync_tile<DIST * C::TILE_OPS>();  // the V part of the last tile landed for every wave
             g2(niter - 1);
         } else {
@@ -1094,6 +1118,7 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
         switch (p.variant) {
         case kVariantDecode: return launch_partial_cfg<64, 1, 1, 8, true>(p, qh, kh, vh, oh, w, l, st);
         case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8, true>(p, qh, kh, vh, oh, w, l, st);
+        case kVariantSmallShared: return launch_partial_cfg<64, 1, 2, 4, true>(p, qh, kh, vh, oh, w, l, st);
         case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4, true>(p, qh, kh, vh, oh, w, l, st);
         default: return (int)hipErrorInvalidValue;
         }

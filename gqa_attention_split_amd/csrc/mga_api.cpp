@@ -50,11 +50,11 @@ int rows_for(int variant) {
 //     double the workgroups. (At an equal, full workgroup count, 64-row tiles
 //     with twice the splits beat 32-row tiles: half the K/V bytes per
 //     workgroup.)
-// Rows M <= 32 take 32-row tiles. The QK-normalised path has only the
-// wave-private 32- and 64-row shapes.
+// Rows M <= 32 take 32-row tiles. The QK-normalised path has only the 32-
+// and 64-row shapes (the 64-row one on the shared ring once keys are split).
 int variant_for(int B, int M, int N, int D, bool qknorm) {
     if (D == 128) return kVariantDecode128;
-    if (qknorm) return M <= 32 ? kVariantDecode : kVariantSmall;  // wave-private rings only
+    if (qknorm) return M <= 32 ? kVariantDecode : kVariantSmall;  // 32 or 64 rows
     if (M <= 32) return kVariantDecode;
     const long long b = B, ms = max_splits(N);
     if (M > 128 && b * ceil_div(M, 256) >= kCUs) return kVariantLarge;
@@ -102,12 +102,12 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);
-    // 64-row tiles over split key ranges run on the shared ring (plain path
-    // only: QK normalisation keeps wave-private rings). With a short key
+    // 64-row tiles over split key ranges run on the shared ring (the plain
+    // and the QK-normalised path alike). With a short key
     // stream per workgroup its smaller end-of-kernel reduction wins (cold
     // A/B: 7% at (16, 256, 4096) x 4 splits and (2, 256, 32768) x 32); an
     // unsplit stream keeps the private ring (2% faster at (64, 256, 4096)).
-    if (!qknorm && p->variant == kVariantSmall && p->splits > 1) p->variant = kVariantSmallShared;
+    if (p->variant == kVariantSmall && p->splits > 1) p->variant = kVariantSmallShared;
     if (N > max_keys(D)) return MGA_ERR_CONFIG;
     const long long groups = ceil_div((long long)B * p->splits, 8) * 8 * p->mtiles;
     if (groups > INT_MAX || (long long)B * M > INT_MAX / D) return MGA_ERR_CONFIG;
