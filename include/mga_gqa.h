@@ -73,7 +73,8 @@ extern "C" {
 typedef enum {
     MGA_OK = 0,
     MGA_ERR_INVALID_VALUE = 1, /* null pointer, B or M < 0, N < 1, splits < 0      */
-    MGA_ERR_LAYOUT = 2,        /* pointer not 16-byte aligned, or N % 8 != 0        */
+    MGA_ERR_LAYOUT = 2,        /* pointer not 16-byte aligned, or a stride the
+                                  strided entry point does not take                 */
     MGA_ERR_CONFIG = 3,        /* D not 64/128, splits > ceil(N / 128), N > 2^30/D - 1,
                                   grid too big                                      */
     MGA_ERR_WORKSPACE = 4,     /* workspace missing, misaligned or too small        */
