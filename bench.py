@@ -258,7 +258,7 @@ def main():
         achieved, peak, unit = flops / sp / 1e12, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"
 
     result = {
-        "metric": "fused GQA exp-sum-div attention TFLOP/s (+ HBM GB/s) on 1 MI355X",
+        "metric": "fused GQA exp-sum-div attention TFLOP/s + HBM GB/s on 1 MI355X",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
