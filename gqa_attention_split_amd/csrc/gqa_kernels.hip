@@ -499,6 +499,14 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)(smem));
     const LaneOffsets<HD> lo = lane_offsets<HD>(lane);
     const TileDma<HD, QW> td = make_tile_dma<HD, QW, KM>(qw, lane, st.k_r, st.v_n);
+    // 32-row query waves on the shared ring: the first query wave of each
+    // stream (the early wave of its SIMD, which waits at each step's barrier
+    // for the late one) issues the stream's whole tile; the late wave issues
+    // no DMA at all.
+    constexpr bool ONE_ISSUER = !C::PRIVATE && QT == 1;
+    constexpr int T1 = 2 * G::DMA;  // DMA instructions per tile of the issuing wave
+    const bool early = wave < C::NWAVES / 2;
+    [[maybe_unused]] const TileDma<HD, 1> td1 = make_tile_dma<HD, 1, KM>(0, lane, st.k_r, st.v_n);
 
     // Tiles are numbered per stream: tile it of stream ks starts at chunk key
     // (it*KS + ks)*32. `ntiles` counts the tiles a stream visits.
@@ -526,7 +534,11 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
     uint32_t vrec = ((uint32_t)(rem0 - 1) * (uint32_t)st.v_n + HD) * 2;
     const uint32_t krec_step = (uint32_t)kstep * 2, vrec_step = (uint32_t)vstep * 2;
     auto issue = [&](int it, uint32_t lds) {  // called for it = 0, 1, 2, ... in order
-        issue_tile<HD, QW>(kcur, krec, vcur, vrec, it < nlive, lds, qw, td);
+        if constexpr (ONE_ISSUER) {
+            if (early) issue_tile<HD, 1>(kcur, krec, vcur, vrec, it < nlive, lds, 0, td1);
+        } else {
+            issue_tile<HD, QW>(kcur, krec, vcur, vrec, it < nlive, lds, qw, td);
+        }
         kcur += kstep;
         vcur += vstep;
         krec -= krec_step;
@@ -722,7 +734,15 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         // Q lands before the tiles after the first are issued (as in the
         // private ring; cold A/B: 1.5% at (16, 256, 4096) and (2, 256, 32768)).
         issue_next();
-        sync_tile<C::TILE_OPS>();  // this wave's Q share landed; barrier: all of Q landed
+        // this wave's Q share landed; barrier: all of Q landed
+        if constexpr (ONE_ISSUER) {
+            if (early)
+                sync_tile<T1>();
+            else
+                sync_tile<0>();
+        } else {
+            sync_tile<C::TILE_OPS>();
+        }
         load_q();                  // done before the first refill overwrites the staging
         for (int j = 1; j < DIST; ++j) issue_next();
 
@@ -782,7 +802,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             // V part of tile it in flight (each wave issues a tile's K
             // instructions before its V instructions; they complete in
             // order, and the barrier makes every wave's share visible).
-            auto sync = [&]() { sync_tile<(DIST - 1) * C::TILE_OPS + C::PER>(); };
+            auto sync = [&]() {
+                if (early)
+                    sync_tile<(DIST - 1) * T1 + T1 / 2>();
+                else
+                    sync_tile<0>();
+            };
             // The scheduling barriers keep the compiler from merging the
             // phases. The orders run in separate loops, so that neither one's
             // live values burden the other's registers.
@@ -826,7 +851,10 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 softmax_last_qkn(niter - 1, s, rk, p);
             else
                 softmax_last(niter - 1, s, p);
-            sync_tile<DIST * C::TILE_OPS>();  // the V part of the last tile landed for every wave
+            if (early)  // the V part of the last tile landed for every wave
+                sync_tile<DIST * T1>();
+            else
+                sync_tile<0>();
             g2(niter - 1);
         } else {
             // Two-stage pipeline, the same order in every wave. Step `it`
