@@ -99,15 +99,34 @@ def time_graph(torch, stream, fn, n_steps, graph_steps, warmup):
     g.replay()  # untimed first replay
     torch.cuda.synchronize()
     reps = max(1, math.ceil(n_steps / graph_steps))
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # One event between consecutive replays (no host synchronisation): the
+    # whole run and each replay's mean per call.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(reps):
+        ev[0].record(stream)
+        for r in range(reps):
             g.replay()
-        end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / (reps * graph_steps), reps * graph_steps
+            ev[r + 1].record(stream)
+    ev[-1].synchronize()
+    per_replay = [ev[r].elapsed_time(ev[r + 1]) / graph_steps for r in range(reps)]
+    return ev[0].elapsed_time(ev[-1]) / (reps * graph_steps), reps * graph_steps, per_replay
+
+
+def gpu_clocks():
+    """Current shader clock and power cap of GPU 0 as rocm-smi reports them
+    (strings), or None where the tool or the field is missing."""
+    import subprocess
+    out = {}
+    for key, flag in (("sclk", "--showclocks"), ("power_cap", "--showmaxpower")):
+        try:
+            r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=20)
+            data = json.loads(r.stdout)
+            card = data.get("card0") or next(iter(data.values()))
+            want = ("sclk", "speed") if key == "sclk" else ("power",)
+            out[key] = next((str(v) for k, v in card.items() if all(w in k.lower() for w in want)), None)
+        except Exception:
+            out[key] = None
+    return out
 
 
 def time_eager(torch, stream, fn, n_steps, warmup):
@@ -216,20 +235,29 @@ def main():
         if rc:
             raise mga.GqaError(rc)
 
-    def timed(fn):
+    replays = {}
+
+    def timed(fn, name=None):
         if args.mode == "graph":
-            return time_graph(torch, stream, fn, args.steps, gsteps, args.warmup)[0]
+            ms, _, per = time_graph(torch, stream, fn, args.steps, gsteps, args.warmup)
+            if name:
+                per = sorted(per)
+                replays[name] = {"n": len(per), "us_per_call_min": round(per[0] * 1e3, 3),
+                                 "us_per_call_median": round(per[len(per) // 2] * 1e3, 3),
+                                 "us_per_call_max": round(per[-1] * 1e3, 3)}
+            return ms
         return time_eager(torch, stream, fn, args.steps, args.warmup)
 
+    clocks_before = gpu_clocks()
     with torch.cuda.stream(stream):
-        ms_step = timed(fwd)
+        ms_step = timed(fwd, "forward")
         timed_steps = args.steps if args.mode == "eager" else \
             max(1, math.ceil(args.steps / gsteps)) * gsteps
         print(f"[bench] forward {ms_step * 1e3:.3f} us/step", file=sys.stderr, flush=True)
         if args.qk_norm:  # no separate entry points: the pair is timed as one
             ms_partial, ms_combine = ms_step, 0.0
         else:
-            ms_partial = timed(partial)
+            ms_partial = timed(partial, "partial_kernel")
             print(f"[bench] partial kernel {ms_partial * 1e3:.3f} us/launch", file=sys.stderr, flush=True)
             ms_combine = timed(combine) if eff > 1 else 0.0
         ms_hot = timed(lambda i: fwd(i, rotate=False))
@@ -242,6 +270,7 @@ def main():
             dst = torch.empty_like(src)
             dst.copy_(src)
     torch.cuda.synchronize()
+    clocks_after = gpu_clocks()
 
     flops = cfg.flops
     alg_bytes = cfg.algorithmic_bytes
@@ -287,6 +316,9 @@ def main():
                      "kernel": "gqa_partial_kernel + gqa_combine_kernel (QK norm)" if args.qk_norm
                      else "gqa_partial_kernel"},
     }
+    if replays:
+        result["replays"] = replays  # spread of the per-replay means within the timed steps
+    result["gpu_clocks"] = {"before": clocks_before, "after": clocks_after}
     if ms_eager is not None:
         result["eager_ms_per_step"] = round(ms_eager, 6)
     if not args.no_cpu_baseline:
