@@ -41,7 +41,8 @@
 //     STAGES tiles per stream, one workgroup barrier per step, and a
 //     two-stage software pipeline: step it runs the first product of tile it
 //     and the second product of tile it-1, with the softmax of one of them
-//     (64-row tiles: the two waves of each SIMD take opposite phases).
+//     (64-row tiles: the two waves of each SIMD take opposite phases, and the
+//     first query wave of each stream issues all of the stream's DMA).
 // After the loop the KS streams of a query group are summed in LDS in a fixed
 // order; with one split the kernel writes O = fp16(W / L), otherwise the
 // normalised partial o_s = fp16(W / L) and L go to the caller's workspace for
@@ -201,6 +202,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *p, uint32_t bytes) {
 // address lds + 16 l. Issued through asm so that the compiler neither waits
 // for these loads before unrelated LDS reads nor reorders memory accesses
 // across them; completion is waited for explicitly (wait_vm / sync_tile).
+// The asm sets m0 (the LDS destination) and lists it as clobbered; clang
+// warns that it does not preserve reserved registers across asm. These
+// kernels have no other m0 user (the generated code sets m0 only inside
+// these asm blocks), so nothing live is lost.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
