@@ -117,6 +117,30 @@ def test_qknorm_extreme_scores_move_the_reference(gpu, D):
         _check(o, q, k, v, f"extreme D{D} s{s}", _eff(q, k, s))
 
 
+def test_qknorm_extreme_scores_on_the_shared_ring(gpu):
+    """64 query rows with split keys run on the shared ring, whose two waves
+    per SIMD take a tile's softmax before or after the previous tile's
+    second product. Rows in both query waves (5 and 40) get keys at -q and
+    +q first and last in the key range; row 45 gets its largest score
+    first; the reference maximum then moves early and late in both phase
+    orders."""
+    B, M, N, D = 2, 64, 3000, 64
+    q, k, v = make_qkv(B, M, N, seed=860, qk_std=1.0, D=D)
+    k = k.copy()
+    for b in range(B):
+        k[b, :, 0] = -q[b, 5]
+        k[b, :, N - 1] = q[b, 5]
+        k[b, :, 1] = -q[b, 40]
+        k[b, :, N - 2] = q[b, 40]
+        k[b, :, 2] = q[b, 45] * np.float16(2.0)
+    for s in (0, 2, 5, 23):
+        plan = mga.mga_gqa_qknorm_plan(B, M, N, D, s)
+        _say(f"[qknorm extreme shared] splits={s} plan={plan}")
+        assert plan[1] == 64 and plan[2] > 1, plan  # 64-row tiles over split keys
+        o = _run(q, k, v, gpu, s)
+        _check(o, q, k, v, f"extreme shared s{s}", _eff(q, k, s))
+
+
 def test_qknorm_strided_any_n_and_structured(gpu):
     import torch
     for D in (64, 128):
