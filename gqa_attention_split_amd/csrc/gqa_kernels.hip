@@ -863,14 +863,16 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             g2(niter - 1);
         } else {
             // Two-stage pipeline, the same order in every wave. Step `it`
-            // reads tile it's K operand, runs the second product of tile it-1
-            // (its V operand read in the previous step, so the MFMAs start
-            // while the K reads are in flight), the first product of tile it,
-            // then reads tile it's V operand and takes tile it's softmax.
-            // Every wave is done with tile it-2 after step it-1, which frees
-            // its buffer for the refill at step it.
+            // reads tile it's K operand and runs the first product of tile it;
+            // then the second product of tile it-1 (its V operand read in the
+            // previous step) and the softmax of tile it go out together, so
+            // that the wave's own VALU work overlaps its second-product MFMAs
+            // (P is double buffered: p holds even tiles, p2 odd ones); last,
+            // it reads tile it's V operand. Every wave is done with tile it-2
+            // after step it-1, which frees its buffer for the refill at
+            // step it.
             float16v s[QT];
-            half8 p[QT][2];
+            half8 p[QT][2], p2[QT][2];
             half8 ka[KSTEPS], va[2][DT];
             auto rk = [&](int it) { load_k(tile_at(it), ka); };
             auto rv = [&](int it) {
@@ -880,12 +882,23 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 read_v<HD>(vbase, va);
             };
             auto mm1 = [&]() { scores<HD, QT>(ka, qf, s); };
-            auto mm2 = [&]() { pv<HD, QT>(va, p, oacc); };
+            auto mm2 = [&](const half8 (&pp)[QT][2]) { pv<HD, QT>(va, pp, oacc); };
             // Tiles before a stream's last (it <= niter - 2) lie inside the chunk.
-            auto sm = [&]() { softmax<QT, false>(s, p, lsum, 0); };
+            auto sm = [&](half8 (&pp)[QT][2]) { softmax<QT, false>(s, pp, lsum, 0); };
             const int niter = ntiles;
-            // The scheduling barriers keep each step's MFMA phase ahead of
-            // its VALU phase.
+            // The scheduling barriers keep the steps' phases in this order.
+            auto step = [&](int it, const half8 (&pin)[QT][2], half8 (&pout)[QT][2]) {
+                sync();
+                rk(it);
+                mm1();
+                issue_next();
+                __builtin_amdgcn_sched_barrier(0);
+                mm2(pin);   // tile it-1
+                sm(pout);   // tile it
+                __builtin_amdgcn_sched_barrier(0);
+                rv(it);
+                __builtin_amdgcn_sched_barrier(0);
+            };
             sync();             // step 0
             rk(0);
             mm1();
@@ -893,29 +906,32 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             __builtin_amdgcn_sched_barrier(0);
             rv(0);
             int it = 1;
+            bool prev_in_p = true;  // P of tile it-1 is in p (else p2)
             if (niter > 1) {
-                sm();
-                for (; it + 1 < niter; ++it) {
-                    sync();
-                    rk(it);
-                    mm2();
-                    mm1();
-                    issue_next();
-                    __builtin_amdgcn_sched_barrier(0);
-                    rv(it);
-                    sm();
-                    __builtin_amdgcn_sched_barrier(0);
+                sm(p);
+                for (; it + 2 < niter; it += 2) {
+                    step(it, p, p2);
+                    step(it + 1, p2, p);
+                }
+                if (it + 1 < niter) {
+                    step(it, p, p2);
+                    ++it;
+                    prev_in_p = false;
                 }
                 sync();         // step niter-1: the last tile's softmax may be masked
                 rk(it);
-                mm2();
                 mm1();
                 issue_next();
+                __builtin_amdgcn_sched_barrier(0);
+                if (prev_in_p)
+                    mm2(p);
+                else
+                    mm2(p2);
                 __builtin_amdgcn_sched_barrier(0);
                 rv(it);
             }
             softmax_last(niter - 1, s, p);
-            mm2();
+            mm2(p);
         }
         sync_tile<0>();  // no DMA in flight, every wave done with the ring
     }
