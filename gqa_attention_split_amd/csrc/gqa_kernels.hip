@@ -830,25 +830,57 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {                      // early
+                // The second product of tile it-1 and the softmax of tile it
+                // share one scheduling region (P double buffered: p holds
+                // even tiles, p2 odd ones).
+                half8 p2[QT][2];
+                auto g2x = [&](int it, const half8 (&pp)[QT][2]) {
+                    half8 a[2][DT];
+                    const char *vbase[DT];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) vbase[dt] = lds_base(smem, tile_at(it) + lo.v[dt]);
+                    read_v<HD>(vbase, a);
+                    pv<HD, QT>(a, pp, oacc);
+                };
+                auto smx = [&](half8 (&pp)[QT][2]) {
+                    if constexpr (QKN)
+                        softmax_qkn<DT, QT, false>(s, rk, rq, pp, lsum, m_run, real, oacc, 0);
+                    else
+                        softmax<QT, false>(s, pp, lsum, 0);
+                };
+                auto estep = [&](int it, const half8 (&pin)[QT][2], half8 (&pout)[QT][2]) {
+                    sync();
+                    g1(it);
+                    issue_next();
+                    __builtin_amdgcn_sched_barrier(0);
+                    g2x(it - 1, pin);
+                    smx(pout);            // tile it
+                    __builtin_amdgcn_sched_barrier(0);
+                };
                 sync();                   // step 0
                 g1(0);
                 issue_next();
                 int it = 1;
                 if (niter > 1) {
-                    sm();
-                    for (; it + 1 < niter; ++it) {
-                        sync();
-                        g1(it);
-                        g2(it - 1);
-                        issue_next();
-                        __builtin_amdgcn_sched_barrier(0);
-                        sm();             // tile it
-                        __builtin_amdgcn_sched_barrier(0);
+                    smx(p);
+                    bool prev_in_p = true;  // P of tile it-1 is in p (else p2)
+                    for (; it + 2 < niter; it += 2) {
+                        estep(it, p, p2);
+                        estep(it + 1, p2, p);
+                    }
+                    if (it + 1 < niter) {
+                        estep(it, p, p2);
+                        ++it;
+                        prev_in_p = false;
                     }
                     sync();               // step niter-1: the last tile's softmax may be masked
                     g1(it);
-                    g2(it - 1);
                     issue_next();
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (prev_in_p)
+                        g2x(it - 1, p);
+                    else
+                        g2x(it - 1, p2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
