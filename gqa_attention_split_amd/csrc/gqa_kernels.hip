@@ -831,56 +831,28 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 }
             } else {                      // early
                 // The second product of tile it-1 and the softmax of tile it
-                // share one scheduling region (P double buffered: p holds
-                // even tiles, p2 odd ones).
-                half8 p2[QT][2];
-                auto g2x = [&](int it, const half8 (&pp)[QT][2]) {
-                    half8 a[2][DT];
-                    const char *vbase[DT];
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) vbase[dt] = lds_base(smem, tile_at(it) + lo.v[dt]);
-                    read_v<HD>(vbase, a);
-                    pv<HD, QT>(a, pp, oacc);
-                };
-                auto smx = [&](half8 (&pp)[QT][2]) {
-                    if constexpr (QKN)
-                        softmax_qkn<DT, QT, false>(s, rk, rq, pp, lsum, m_run, real, oacc, 0);
-                    else
-                        softmax<QT, false>(s, pp, lsum, 0);
-                };
-                auto estep = [&](int it, const half8 (&pin)[QT][2], half8 (&pout)[QT][2]) {
-                    sync();
-                    g1(it);
-                    issue_next();
-                    __builtin_amdgcn_sched_barrier(0);
-                    g2x(it - 1, pin);
-                    smx(pout);            // tile it
-                    __builtin_amdgcn_sched_barrier(0);
-                };
+                // share one scheduling region (one P buffer: the softmax's
+                // conversions into P wait for the MFMAs that read it).
                 sync();                   // step 0
                 g1(0);
                 issue_next();
                 int it = 1;
                 if (niter > 1) {
-                    smx(p);
-                    bool prev_in_p = true;  // P of tile it-1 is in p (else p2)
-                    for (; it + 2 < niter; it += 2) {
-                        estep(it, p, p2);
-                        estep(it + 1, p2, p);
-                    }
-                    if (it + 1 < niter) {
-                        estep(it, p, p2);
-                        ++it;
-                        prev_in_p = false;
+                    sm();
+                    for (; it + 1 < niter; ++it) {
+                        sync();
+                        g1(it);
+                        issue_next();
+                        __builtin_amdgcn_sched_barrier(0);
+                        g2(it - 1);
+                        sm();             // tile it
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                     sync();               // step niter-1: the last tile's softmax may be masked
                     g1(it);
                     issue_next();
                     __builtin_amdgcn_sched_barrier(0);
-                    if (prev_in_p)
-                        g2x(it - 1, p);
-                    else
-                        g2x(it - 1, p2);
+                    g2(it - 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -899,12 +871,12 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             // then the second product of tile it-1 (its V operand read in the
             // previous step) and the softmax of tile it go out together, so
             // that the wave's own VALU work overlaps its second-product MFMAs
-            // (P is double buffered: p holds even tiles, p2 odd ones); last,
-            // it reads tile it's V operand. Every wave is done with tile it-2
-            // after step it-1, which frees its buffer for the refill at
-            // step it.
+            // (one P buffer: the softmax's conversions into P wait for the
+            // MFMAs that read it, its exps need not); last, it reads tile
+            // it's V operand. Every wave is done with tile it-2 after step
+            // it-1, which frees its buffer for the refill at step it.
             float16v s[QT];
-            half8 p[QT][2], p2[QT][2];
+            half8 p[QT][2];
             half8 ka[KSTEPS], va[2][DT];
             auto rk = [&](int it) { load_k(tile_at(it), ka); };
             auto rv = [&](int it) {
@@ -914,23 +886,11 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 read_v<HD>(vbase, va);
             };
             auto mm1 = [&]() { scores<HD, QT>(ka, qf, s); };
-            auto mm2 = [&](const half8 (&pp)[QT][2]) { pv<HD, QT>(va, pp, oacc); };
+            auto mm2 = [&]() { pv<HD, QT>(va, p, oacc); };
             // Tiles before a stream's last (it <= niter - 2) lie inside the chunk.
-            auto sm = [&](half8 (&pp)[QT][2]) { softmax<QT, false>(s, pp, lsum, 0); };
+            auto sm = [&]() { softmax<QT, false>(s, p, lsum, 0); };
             const int niter = ntiles;
             // The scheduling barriers keep the steps' phases in this order.
-            auto step = [&](int it, const half8 (&pin)[QT][2], half8 (&pout)[QT][2]) {
-                sync();
-                rk(it);
-                mm1();
-                issue_next();
-                __builtin_amdgcn_sched_barrier(0);
-                mm2(pin);   // tile it-1
-                sm(pout);   // tile it
-                __builtin_amdgcn_sched_barrier(0);
-                rv(it);
-                __builtin_amdgcn_sched_barrier(0);
-            };
             sync();             // step 0
             rk(0);
             mm1();
@@ -938,32 +898,31 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             __builtin_amdgcn_sched_barrier(0);
             rv(0);
             int it = 1;
-            bool prev_in_p = true;  // P of tile it-1 is in p (else p2)
             if (niter > 1) {
-                sm(p);
-                for (; it + 2 < niter; it += 2) {
-                    step(it, p, p2);
-                    step(it + 1, p2, p);
-                }
-                if (it + 1 < niter) {
-                    step(it, p, p2);
-                    ++it;
-                    prev_in_p = false;
+                sm();
+                for (; it + 1 < niter; ++it) {
+                    sync();
+                    rk(it);
+                    mm1();
+                    issue_next();
+                    __builtin_amdgcn_sched_barrier(0);
+                    mm2();      // tile it-1
+                    sm();       // tile it
+                    __builtin_amdgcn_sched_barrier(0);
+                    rv(it);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 sync();         // step niter-1: the last tile's softmax may be masked
                 rk(it);
                 mm1();
                 issue_next();
                 __builtin_amdgcn_sched_barrier(0);
-                if (prev_in_p)
-                    mm2(p);
-                else
-                    mm2(p2);
+                mm2();
                 __builtin_amdgcn_sched_barrier(0);
                 rv(it);
             }
             softmax_last(niter - 1, s, p);
-            mm2(p);
+            mm2();
         }
         sync_tile<0>();  // no DMA in flight, every wave done with the ring
     }
