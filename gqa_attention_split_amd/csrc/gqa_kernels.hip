@@ -769,11 +769,13 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
         if constexpr (QT == 1) {
             // Two-stage pipeline with a phase offset. Step `it` runs the first
             // product of tile it, the second product of tile it-1 and one
-            // softmax: of tile it in an early wave (after the products), of
-            // tile it-1 in a late wave (before them). The two waves of a SIMD
-            // are one early (w < NWAVES/2) and one late (w + NWAVES/2): the
-            // barrier of each step starts both together, and then one issues
-            // MFMAs while the other issues VALU.
+            // softmax: of tile it in an early wave (after its first product,
+            // beside its second), of tile it-1 in a late wave (before both
+            // products). The two waves of a SIMD are one early
+            // (w < NWAVES/2) and one late (w + NWAVES/2): the barrier of each
+            // step starts both together, and then one issues MFMAs while the
+            // other issues VALU. The early wave, the stream's first query
+            // wave, also issues the stream's DMA.
             float16v s[QT];
             half8 p[QT][2];
             [[maybe_unused]] float16v rk;  // QK normalisation: the key scales of the tile in s
@@ -803,10 +805,11 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             };
             const int niter = ntiles;
             // Step it needs the K part of tile it and the V part of tile
-            // it-1, which was issued before it: the step's wait leaves the
-            // V part of tile it in flight (each wave issues a tile's K
-            // instructions before its V instructions; they complete in
-            // order, and the barrier makes every wave's share visible).
+            // it-1, which was issued before it: the early wave's wait leaves
+            // the V part of tile it in flight (it issues a tile's K
+            // instructions before its V instructions and they complete in
+            // order); the late wave issues no DMA and waits only at the
+            // barrier, which makes the tile visible to it.
             auto sync = [&]() {
                 if (early)
                     sync_tile<(DIST - 1) * T1 + T1 / 2>();
