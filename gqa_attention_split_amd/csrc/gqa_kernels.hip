@@ -632,7 +632,17 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             real[qt] = false;
         }
     }
-    auto key_scales = [&](const half8 (&ka)[KSTEPS], float16v &rk) {
+    auto scales_from_slot = [&](const float *slot, float16v &rk) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4v t = *reinterpret_cast<const float4v *>(slot + 8 * g + 4 * h);
+            rk[4 * g] = t[0];
+            rk[4 * g + 1] = t[1];
+            rk[4 * g + 2] = t[2];
+            rk[4 * g + 3] = t[3];
+        }
+    };
+    auto key_scales_at = [&](const half8 (&ka)[KSTEPS], float16v &rk, float *slot) {
         float ss = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
@@ -643,16 +653,11 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             }
         ss += __shfl_xor(ss, 32);
         const float r = __builtin_amdgcn_rsqf(ss * (1.f / HD) + eps);
-        float *slot = reinterpret_cast<float *>(smem + C::SCR_OFF + wave * 128);
         if (h == 0) slot[lane & 31] = r;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4v t = *reinterpret_cast<const float4v *>(slot + 8 * g + 4 * h);
-            rk[4 * g] = t[0];
-            rk[4 * g + 1] = t[1];
-            rk[4 * g + 2] = t[2];
-            rk[4 * g + 3] = t[3];
-        }
+        scales_from_slot(slot, rk);
+    };
+    auto key_scales = [&](const half8 (&ka)[KSTEPS], float16v &rk) {
+        key_scales_at(ka, rk, reinterpret_cast<float *>(smem + C::SCR_OFF + wave * 128));
     };
 
     // Softmax numerators of a stream's last tile, the only one that can reach
@@ -779,11 +784,19 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
             float16v s[QT];
             half8 p[QT][2];
             [[maybe_unused]] float16v rk;  // QK normalisation: the key scales of the tile in s
+            // QK normalisation: the early wave computes each tile's key scales
+            // into its stream's slot (two per stream, by tile parity); the
+            // late wave, which takes tile it's softmax one step later, reads
+            // them from there.
+            [[maybe_unused]] auto kslot = [&](int it) {
+                return reinterpret_cast<float *>(smem + C::SCR_OFF + (ks * 2 + (it & 1)) * 128);
+            };
             auto g1 = [&](int it) {
                 half8 a[KSTEPS];
                 load_k(tile_at(it), a);
                 scores<HD, QT>(a, qf, s);
-                if constexpr (QKN) key_scales(a, rk);
+                if constexpr (QKN)
+                    if (early) key_scales_at(a, rk, kslot(it));
             };
             // Tiles before a stream's last (it <= niter - 2) lie inside the chunk.
             // With QK normalisation the softmax may rescale W and L: in either
@@ -825,6 +838,7 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                 issue_next();
                 for (int it = 1; it < niter; ++it) {
                     sync();
+                    if constexpr (QKN) scales_from_slot(kslot(it - 1), rk);
                     sm();                 // tile it-1
                     __builtin_amdgcn_sched_barrier(0);
                     g1(it);
@@ -859,14 +873,23 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            if constexpr (QKN)
-                softmax_last_qkn(niter - 1, s, rk, p);
-            else
+            // The late wave reads the last tile's key scales after the
+            // barrier below: the early wave writes them in its last step.
+            if constexpr (QKN) {
+                if (early) softmax_last_qkn(niter - 1, s, rk, p);
+            } else {
                 softmax_last(niter - 1, s, p);
+            }
             if (early)  // the V part of the last tile landed for every wave
                 sync_tile<DIST * T1>();
             else
                 sync_tile<0>();
+            if constexpr (QKN) {
+                if (!early) {
+                    scales_from_slot(kslot(niter - 1), rk);
+                    softmax_last_qkn(niter - 1, s, rk, p);
+                }
+            }
             g2(niter - 1);
         } else {
             // Two-stage pipeline, the same order in every wave. Step `it`
