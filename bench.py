@@ -112,23 +112,6 @@ def time_graph(torch, stream, fn, n_steps, graph_steps, warmup):
     return ev[0].elapsed_time(ev[-1]) / (reps * graph_steps), reps * graph_steps, per_replay
 
 
-def gpu_clocks():
-    """Current shader clock and power cap of GPU 0 as rocm-smi reports them
-    (strings), or None where the tool or the field is missing."""
-    import subprocess
-    out = {}
-    for key, flag in (("sclk", "--showclocks"), ("power_cap", "--showmaxpower")):
-        try:
-            r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True, timeout=20)
-            data = json.loads(r.stdout)
-            card = data.get("card0") or next(iter(data.values()))
-            want = ("sclk", "speed") if key == "sclk" else ("power",)
-            out[key] = next((str(v) for k, v in card.items() if all(w in k.lower() for w in want)), None)
-        except Exception:
-            out[key] = None
-    return out
-
-
 def time_eager(torch, stream, fn, n_steps, warmup):
     for i in range(warmup):
         fn(i)
@@ -248,7 +231,6 @@ def main():
             return ms
         return time_eager(torch, stream, fn, args.steps, args.warmup)
 
-    clocks_before = gpu_clocks()
     with torch.cuda.stream(stream):
         ms_step = timed(fwd, "forward")
         timed_steps = args.steps if args.mode == "eager" else \
@@ -270,7 +252,6 @@ def main():
             dst = torch.empty_like(src)
             dst.copy_(src)
     torch.cuda.synchronize()
-    clocks_after = gpu_clocks()
 
     flops = cfg.flops
     alg_bytes = cfg.algorithmic_bytes
@@ -318,7 +299,6 @@ def main():
     }
     if replays:
         result["replays"] = replays  # spread of the per-replay means within the timed steps
-    result["gpu_clocks"] = {"before": clocks_before, "after": clocks_after}
     if ms_eager is not None:
         result["eager_ms_per_step"] = round(ms_eager, 6)
     if not args.no_cpu_baseline:

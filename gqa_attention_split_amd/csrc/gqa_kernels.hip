@@ -1190,7 +1190,10 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
         }
     }
     switch (p.variant) {
-    case kVariantDecode: return launch_partial_cfg<64, 1, 1, 8>(p, qh, kh, vh, oh, w, l, st);
+    // 32 rows on 4 waves (two workgroups per CU): cold A/B against 8 waves at
+    // 4 splits, (64, 8, 8192) 30.05 -> 28.17 us at 8 splits, (2, 256, 4096)
+    // 8.45 -> 7.57 us.
+    case kVariantDecode: return launch_partial_cfg<64, 1, 1, 4>(p, qh, kh, vh, oh, w, l, st);
     case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8>(p, qh, kh, vh, oh, w, l, st);
     case kVariantMedium: return launch_partial_cfg<64, 2, 2, 4>(p, qh, kh, vh, oh, w, l, st);
     case kVariantLarge: return launch_partial_cfg<64, 2, 4, 2>(p, qh, kh, vh, oh, w, l, st);

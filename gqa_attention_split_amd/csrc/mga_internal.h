@@ -33,8 +33,10 @@ struct Plan {
 };
 
 // Kernel shapes: (query tiles of 32 per wave, query waves, key streams).
-// Every shape has 8 waves per workgroup (two per SIMD).
-constexpr int kVariantDecode = 0;  // (1, 1, 8),  32 rows per workgroup, wave-private rings
+// Shapes have 8 waves per workgroup (two per SIMD) except the plain 32-row one
+// (4 waves; two such workgroups share a CU) and head dim 128 (4 waves).
+constexpr int kVariantDecode = 0;  // (1, 1, 4),  32 rows per workgroup, 4 waves, wave-private rings
+                                   // (QK norm: (1, 1, 8), 8 waves)
 constexpr int kVariantSmall = 1;   // (2, 1, 8),  64 rows per workgroup, wave-private rings
 constexpr int kVariantMedium = 2;  // (2, 2, 4), 128 rows per workgroup, shared ring
 constexpr int kVariantLarge = 3;   // (2, 4, 2), 256 rows per workgroup, shared ring

@@ -142,7 +142,7 @@ def test_split_policy_and_workspace(B, M, N, D):
     (16, 256, 4096, 64, 64, 4),      # 64-row tiles, 4 splits fill 256 CUs
     (2, 256, 4096, 64, 32, 8),       # 64-row tiles would reach 64 workgroups at most: 32-row tiles
     (2, 256, 32768, 64, 64, 32),
-    (64, 8, 8192, 64, 32, 4),        # decode-like rows: 32-row tiles
+    (64, 8, 8192, 64, 32, 8),        # decode-like rows: 32-row tiles, 4 waves, two workgroups per CU
     (128, 256, 16384, 64, 128, 1),   # 128-row tiles fill the chip unsplit
     (70, 300, 16384, 64, 256, 2),    # 256-row tiles fill the chip with two splits (128-row do not unsplit)
     (128, 130, 520, 64, 128, 1),     # 128-row tiles fill the chip unsplit
