@@ -112,6 +112,38 @@ def time_graph(torch, stream, fn, n_steps, graph_steps, warmup):
     return ev[0].elapsed_time(ev[-1]) / (reps * graph_steps), reps * graph_steps, per_replay
 
 
+def gpu_clocks():
+    """Shader clock and power cap of the AMD cards, read from sysfs (plain file
+    reads: no child process). Each entry: the card, the current `pp_dpm_sclk`
+    level (MHz) and the hwmon power cap (W); None where the files are absent."""
+    out = []
+    base = "/sys/class/drm"
+    try:
+        cards = sorted(c for c in os.listdir(base) if re.fullmatch(r"card\d+", c))
+    except OSError:
+        return None
+    for c in cards:
+        dev = os.path.join(base, c, "device")
+        try:
+            if open(os.path.join(dev, "vendor")).read().strip() != "0x1002":
+                continue
+            sclk = None
+            for line in open(os.path.join(dev, "pp_dpm_sclk")):
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    sclk = int(m.group(1)) if m else None
+            cap = None
+            hw = os.path.join(dev, "hwmon")
+            for h in sorted(os.listdir(hw)) if os.path.isdir(hw) else []:
+                f = os.path.join(hw, h, "power1_cap")
+                if os.path.exists(f):
+                    cap = round(int(open(f).read()) / 1e6, 1)
+            out.append({"card": c, "sclk_mhz": sclk, "power_cap_w": cap})
+        except (OSError, ValueError):
+            continue
+    return out or None
+
+
 def time_eager(torch, stream, fn, n_steps, warmup):
     for i in range(warmup):
         fn(i)
@@ -231,11 +263,13 @@ def main():
             return ms
         return time_eager(torch, stream, fn, args.steps, args.warmup)
 
+    clocks_before = gpu_clocks()
     with torch.cuda.stream(stream):
         ms_step = timed(fwd, "forward")
         timed_steps = args.steps if args.mode == "eager" else \
             max(1, math.ceil(args.steps / gsteps)) * gsteps
         print(f"[bench] forward {ms_step * 1e3:.3f} us/step", file=sys.stderr, flush=True)
+        clocks_after = gpu_clocks()  # just after the forward's timed region
         if args.qk_norm:  # no separate entry points: the pair is timed as one
             ms_partial, ms_combine = ms_step, 0.0
         else:
@@ -297,6 +331,7 @@ def main():
                      "kernel": "gqa_partial_kernel + gqa_combine_kernel (QK norm)" if args.qk_norm
                      else "gqa_partial_kernel"},
     }
+    result["gpu_clocks"] = {"before": clocks_before, "after": clocks_after}
     if replays:
         result["replays"] = replays  # spread of the per-replay means within the timed steps
     if ms_eager is not None:
