@@ -185,7 +185,7 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build measures one GPU only (asked for {max(args.gpus, world)}); "
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}); "
               "the fused GQA path shards over the batch axis with no exchange, but no "
               "multi-GPU run is part of it.", file=sys.stderr)
         sys.exit(2)
