@@ -1198,7 +1198,11 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
     case kVariantMedium: return launch_partial_cfg<64, 2, 2, 4>(p, qh, kh, vh, oh, w, l, st);
     case kVariantLarge: return launch_partial_cfg<64, 2, 4, 2>(p, qh, kh, vh, oh, w, l, st);
     case kVariantSmallShared: return launch_partial_cfg<64, 1, 2, 4>(p, qh, kh, vh, oh, w, l, st);
-    case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4>(p, qh, kh, vh, oh, w, l, st);
+    // Head dim 128 on 2 waves (one workgroup per CU at the policy's splits,
+    // each wave streaming twice the tiles): cold A/B against 4 waves,
+    // (64, 1, 4096) 29.65 -> 28.3 us, (16, 1, 16384) 30.76 -> 29.26,
+    // (64, 32, 4096) 30.00 -> 28.85.
+    case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 2>(p, qh, kh, vh, oh, w, l, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
