@@ -1182,10 +1182,14 @@ int launch_partial(const Plan &p, const void *q, const void *k, const void *v, v
     _Float16 *oh = (_Float16 *)o;
     if (p.qknorm) {
         switch (p.variant) {
-        case kVariantDecode: return launch_partial_cfg<64, 1, 1, 8, true>(p, qh, kh, vh, oh, w, l, st);
+        // 32 rows on 4 waves (two workgroups per CU) and head dim 128 on 2
+        // waves, as in the plain path: cold A/B against 8 and 4 waves,
+        // (64, 8, 8192) 32.00 -> 30.80 us (4 -> 8 splits), (64, 1, 4096, 128)
+        // 32.81 -> 30.18, (16, 1, 16384, 128) 34.66 -> 32.24.
+        case kVariantDecode: return launch_partial_cfg<64, 1, 1, 4, true>(p, qh, kh, vh, oh, w, l, st);
         case kVariantSmall: return launch_partial_cfg<64, 2, 1, 8, true>(p, qh, kh, vh, oh, w, l, st);
         case kVariantSmallShared: return launch_partial_cfg<64, 1, 2, 4, true>(p, qh, kh, vh, oh, w, l, st);
-        case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 4, true>(p, qh, kh, vh, oh, w, l, st);
+        case kVariantDecode128: return launch_partial_cfg<128, 1, 1, 2, true>(p, qh, kh, vh, oh, w, l, st);
         default: return (int)hipErrorInvalidValue;
         }
     }

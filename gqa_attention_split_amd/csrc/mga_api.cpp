@@ -64,19 +64,19 @@ int variant_for(int B, int M, int N, int D, bool qknorm) {
     return kVariantDecode;
 }
 
-// Workgroups of a shape that fit one compute unit at once: the plain 32-row
-// shape has 4 waves and 68 KB of LDS, so two fit; every other shape takes a
-// whole CU.
-long long wgs_per_cu(int variant, bool qknorm) { return variant == kVariantDecode && !qknorm ? 2 : 1; }
+// Workgroups of a shape that fit one compute unit at once: the 32-row shape
+// has 4 waves and 64-70 KB of LDS (with or without QK norm), so two fit;
+// every other shape takes a whole CU at the policy's split counts.
+long long wgs_per_cu(int variant) { return variant == kVariantDecode ? 2 : 1; }
 
 // Policy: split the keys just enough that the grid fills every compute unit
 // (one or two workgroups each), keeping at least kMinChunkBlocks key blocks
 // per split where N allows (shorter chunks cost more in partial traffic and
 // combine work than the extra workgroups gain).
-int policy_splits(int B, int M, int N, int variant, bool qknorm) {
+int policy_splits(int B, int M, int N, int variant) {
     if (N < 1 || B < 1 || M < 1) return 1;
     const long long base = (long long)B * ceil_div(M, rows_for(variant));
-    const long long s = std::min(ceil_div(kCUs * wgs_per_cu(variant, qknorm), base), max_splits(N));
+    const long long s = std::min(ceil_div(kCUs * wgs_per_cu(variant), base), max_splits(N));
     return (int)std::max(1LL, s);
 }
 
@@ -103,7 +103,7 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     p->nblocks = (int)nblocks;
     p->key_major = false;
     p->st = Strides{(long long)M * D, (long long)D * N, (long long)N * D, (long long)M * D, D, N, D, D};
-    const int want = splits == 0 ? policy_splits(B, M, N, p->variant, qknorm) : splits;
+    const int want = splits == 0 ? policy_splits(B, M, N, p->variant) : splits;
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);

@@ -33,16 +33,14 @@ struct Plan {
 };
 
 // Kernel shapes: (query tiles of 32 per wave, query waves, key streams).
-// Shapes have 8 waves per workgroup (two per SIMD) except the plain 32-row one
-// (4 waves; two such workgroups share a CU) and head dim 128 (2 waves plain,
-// 4 with QK norm).
+// Shapes have 8 waves per workgroup (two per SIMD) except the 32-row one
+// (4 waves; two such workgroups share a CU) and head dim 128 (2 waves).
 constexpr int kVariantDecode = 0;  // (1, 1, 4),  32 rows per workgroup, 4 waves, wave-private rings
-                                   // (QK norm: (1, 1, 8), 8 waves)
 constexpr int kVariantSmall = 1;   // (2, 1, 8),  64 rows per workgroup, wave-private rings
 constexpr int kVariantMedium = 2;  // (2, 2, 4), 128 rows per workgroup, shared ring
 constexpr int kVariantLarge = 3;   // (2, 4, 2), 256 rows per workgroup, shared ring
 // Head dim 128: (1, 1, 2), 32 rows per workgroup, 2 waves with wave-private
-// rings of two 16 KiB tiles (QK norm: (1, 1, 4), 4 waves).
+// rings of two 16 KiB tiles.
 constexpr int kVariantDecode128 = 4;
 // (1, 2, 4): 64 rows per workgroup on a shared ring, for split key ranges:
 // its cross-stream reduction sums 4 streams of 32-row partials, not 8 of
