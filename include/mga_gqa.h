@@ -118,8 +118,9 @@ size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
  * tile alone gives at least 256 workgroups (one per compute unit), else 256
  * rows when two splits do, else 64 rows, or 32 rows when even the most splits
  * leave 64-row tiles short of 256 workgroups (and always for M <= 32);
- * D = 128: 32 rows. Splits then bring the grid to 256 workgroups, each
- * keeping at least 4 blocks of 128 keys. Either output pointer
+ * D = 128: 32 rows. Splits then bring the grid to 256 workgroups (512 for
+ * 32-row tiles at D = 64, two of which share a compute unit), each keeping
+ * at least 4 blocks of 128 keys. Either output pointer
  * may be NULL. Returns MGA_OK, INVALID_VALUE or CONFIG for the shape; the
  * memory layout is not part of the plan. */
 int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
