@@ -158,6 +158,18 @@ def time_eager(torch, stream, fn, n_steps, warmup):
     return start.elapsed_time(end) / n_steps
 
 
+def eager_per_call(torch, stream, fn, n_steps):
+    """Per-call durations (ms) of n_steps back-to-back eager calls: one event
+    between consecutive calls on `stream`, no host synchronisation inside."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    ev[0].record(stream)
+    for i in range(n_steps):
+        fn(i)
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n_steps))
+
+
 def cpu_baseline(cfg, q, k, v, target_s):
     """The oracle as it stands, on the host's cores, over the whole workload
     (every batch row, query row and key), repeated until about `target_s`
@@ -279,6 +291,7 @@ def main():
         ms_hot = timed(lambda i: fwd(i, rotate=False))
         ms_eager = time_eager(torch, stream, fwd, args.steps, args.warmup) \
             if args.eager and args.mode == "graph" else None
+        per_call = eager_per_call(torch, stream, fwd, args.steps) if args.eager else None
         if args.pmc_calibrate:
             # One plain device-to-device copy of known size: the reference
             # dispatch that FETCH_SIZE / WRITE_SIZE readings are scaled by.
@@ -336,6 +349,9 @@ def main():
         result["replays"] = replays  # spread of the per-replay means within the timed steps
     if ms_eager is not None:
         result["eager_ms_per_step"] = round(ms_eager, 6)
+    if per_call:
+        pc = lambda f: round(per_call[min(len(per_call) - 1, int(f * len(per_call)))] * 1e3, 3)
+        result["eager_us_per_call"] = {"p10": pc(0.1), "median": pc(0.5), "p90": pc(0.9)}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
         cb["value"] = round(cb["value"], 6)
