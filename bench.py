@@ -182,6 +182,19 @@ def cpu_baseline(cfg, q, k, v, target_s):
         t_total += time.perf_counter() - t0
         reps += 1
     dt = t_total / reps
+    # The same oracle on one thread, one call (bounded: a few seconds at the
+    # largest workloads' batch sizes would be minutes, so only when the
+    # all-thread call took under 0.5 s).
+    one = None
+    n_all = oracle.threads()
+    if dt < 0.5 and n_all > 1:
+        oracle.set_threads(1)
+        try:
+            t0 = time.perf_counter()
+            oracle.gqa_f64(q, k, v)
+            one = time.perf_counter() - t0
+        finally:
+            oracle.set_threads(n_all)
     return {
         "value": cfg.flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -190,6 +203,7 @@ def cpu_baseline(cfg, q, k, v, target_s):
         "sample": (f"whole workload ({cfg.B}x{cfg.M} query rows x {cfg.N} keys, "
                    f"{cfg.flops / 1e9:.2f} GFLOP) x {reps} repeats, {dt:.3f} s each; "
                    "fp64 C loops, OpenMP over query rows"),
+        **({"value_1thread": cfg.flops / one / 1e12} if one else {}),
     }
 
 
@@ -355,6 +369,10 @@ def main():
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
         cb["value"] = round(cb["value"], 6)
+        one = cb.pop("value_1thread", None)
+        if one is not None:  # the oracle on one core, one call of the same workload
+            result["cpu_baseline_1thread"] = {"value": round(one, 6), "unit": cb["unit"], "cores": 1,
+                                              "kind": "oracle"}
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 

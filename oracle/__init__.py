@@ -68,6 +68,8 @@ def _load():
         lib.mga_oracle_gqa_f64.restype = ctypes.c_int
         lib.mga_oracle_threads.argtypes = []
         lib.mga_oracle_threads.restype = ctypes.c_int
+        lib.mga_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.mga_oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -75,6 +77,12 @@ def _load():
 def threads() -> int:
     """OpenMP threads the C oracle runs with (OMP_NUM_THREADS or all cores)."""
     return int(_load().mga_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for later calls of the C oracle (n >= 1); for timing on
+    one core. Results do not depend on it."""
+    _load().mga_oracle_set_threads(int(n))
 
 
 def _as_f64(x) -> np.ndarray:

@@ -32,6 +32,19 @@
 #include <omp.h>
 #endif
 
+/* Thread count for later calls (n >= 1); used to time the oracle on one
+ * core. Changes no arithmetic: each output row is computed by one thread in
+ * the same order whatever the count. */
+void mga_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int mga_oracle_threads(void)
 {
 #ifdef _OPENMP

@@ -47,3 +47,23 @@ def test_traffic_only_from_the_current_source(tmp_path, monkeypatch):
     _profile(tmp_path, cur, "gqa_b2_m256_n4096", 2.5e7)
     assert bench.read_traffic("gqa_b16_m256_n4096") is None
     assert bench.read_traffic("gqa_b64_m8_n8192") is None   # no summary at all
+
+
+def test_oracle_thread_count_changes_no_result():
+    """The single-core timing of the CPU baseline sets the oracle's thread
+    count; every output row is one thread's work in a fixed order, so the
+    bits do not depend on it."""
+    import numpy as np
+    import oracle
+    from gqa_attention_split_amd.inputs import make_qkv
+    q, k, v = make_qkv(2, 40, 300, seed=5)
+    n_all = oracle.threads()
+    a = oracle.gqa_f64(q, k, v)
+    oracle.set_threads(1)
+    try:
+        b = oracle.gqa_f64(q, k, v)
+        assert oracle.threads() == 1
+    finally:
+        oracle.set_threads(n_all)
+    assert oracle.threads() == n_all
+    assert np.array_equal(a, b)
