@@ -1059,7 +1059,8 @@ __global__ __launch_bounds__(64 * QW * KS) void gqa_partial_kernel(
 }
 
 // Combine: HD/4 threads per output row, 4 head dims each.
-// O = fp16(sum_s L_s o_s / sum_s L_s), both sums in split order.
+// O = fp16(sum_s L_s o_s / sum_s L_s), both sums in split order (from 32
+// splits, the grouped form below sums four quarters, then the quarters).
 // With LSE (QK normalisation) the workspace holds lse_s = log2 of each
 // split's weight mass; the weights are then 2^(lse_s - max_s lse_s).
 // The partials sit in L2 or the Infinity Cache and each thread is bound by
@@ -1120,6 +1121,59 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(acc[i] / l);
     const long long b = row / M;
     *reinterpret_cast<half4 *>(o + b * o_b + (row - b * M) * o_i + 4 * c) = hv;
+}
+
+// Combine over many splits, plain graph: few rows (a long key range on a
+// small batch) leave the one-thread-per-4-columns form with few workgroups,
+// each walking every split in turn. Here four groups of 64 threads share the
+// same rows: group g sums the g-th contiguous quarter of the splits in split
+// order, and group 0 then adds groups 1, 2, 3 in that order (fixed, so the
+// result is deterministic) before the division.
+template <int HD>
+__global__ __launch_bounds__(256) void gqa_combine_grouped_kernel(const _Float16 *__restrict__ ws_o,
+                                                                  const float *__restrict__ ws_l,
+                                                                  _Float16 *__restrict__ o, long long o_b,
+                                                                  int o_i, int M, long long rows, int nsplit) {
+    constexpr int CPR = HD / 4;    // threads per row, 4 head dims each
+    constexpr int RPB = 64 / CPR;  // rows per workgroup
+    __shared__ float red[3][5][64];
+    const int g = threadIdx.x >> 6, t = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * RPB + t / CPR;
+    const int c = t % CPR;
+    const bool valid = row < rows;
+    const int s0 = g * nsplit / 4, s1 = (g + 1) * nsplit / 4;
+    float l = 0.f;
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+#pragma unroll 8
+        for (int s = s0; s < s1; ++s) {
+            const long long prow = (long long)s * rows + row;
+            const float w = ws_l[prow];
+            const half4 os = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
+            l += w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += w * (float)os[i];
+        }
+    }
+    if (g > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[g - 1][i][t] = acc[i];
+        red[g - 1][4][t] = l;
+    }
+    __syncthreads();
+    if (g == 0 && valid) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            l += red[j][4][t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += red[j][i][t];
+        }
+        half4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(acc[i] / l);
+        const long long b = row / M;
+        *reinterpret_cast<half4 *>(o + b * o_b + (row - b * M) * o_i + 4 * c) = hv;
+    }
 }
 
 // K repack for contiguous head-dim-major K whose rows (N keys) are not
@@ -1230,6 +1284,17 @@ int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
     const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
     hipStream_t st = (hipStream_t)stream;
     _Float16 *oh = (_Float16 *)o;
+    if (!p.qknorm && p.splits >= kGroupedCombineSplits) {
+        const long long rpb = 64 / (p.D / 4);
+        const dim3 ggrid((unsigned)((rows + rpb - 1) / rpb));
+        if (p.D == 128)
+            hipLaunchKernelGGL((gqa_combine_grouped_kernel<128>), ggrid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
+                               p.st.o_i, p.M, rows, p.splits);
+        else
+            hipLaunchKernelGGL((gqa_combine_grouped_kernel<64>), ggrid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
+                               p.st.o_i, p.M, rows, p.splits);
+        return (int)hipGetLastError();
+    }
     if (p.D == 128 && p.qknorm)
         hipLaunchKernelGGL((gqa_combine_kernel<128, true>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
                            p.st.o_i, p.M, rows, p.splits);

@@ -52,6 +52,14 @@ constexpr int kKeyBlock = 128;
 // D * N * 2 bytes stay below 2^31.
 constexpr int max_keys(int D) { return (1 << 30) / D - 1; }
 constexpr int kThreads = 256;
+// Split count from which the plain combine runs four split groups per
+// workgroup (gqa_combine_grouped_kernel, which needs kThreads == 256). Cold
+// A/B, us per forward: (2, 256, 32768) at 32 splits 16.10 -> 14.53; at 8
+// splits (2, 256, 4096) 7.54 -> 7.77 and (64, 8, 8192) 27.89 -> 28.26, at 16
+// splits (16, 1, 16384, 128) 29.20 -> 29.46, so fewer splits keep the
+// one-group form.
+constexpr int kGroupedCombineSplits = 32;
+static_assert(kThreads == 256, "grouped combine: four groups of 64 threads");
 
 // Fills `p` for a call; returns an mga_status (0 = ok). Host only, no HIP calls.
 // The layout is left contiguous and unchecked; set_layout fixes it. With

@@ -181,7 +181,8 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
 
 /* Only the combine kernel:
  *     O[b,i,:] = fp16(sum_s L[s,b,i] o[s,b,i,:] / sum_s L[s,b,i])
- * with the sums taken in split order (fp32). `ws` holds the partials a preceding
+ * with the sums taken in fp32 in a fixed order (split order; from 32 splits,
+ * four contiguous quarters in split order, then the quarters in order). `ws` holds the partials a preceding
  * mga_gqa_partial call wrote for the same (B, M, N, splits); q, k and v are
  * not read. A no-op returning MGA_OK when the effective split count is 1. */
 int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits,
