@@ -1123,13 +1123,15 @@ __global__ __launch_bounds__(256) void gqa_combine_kernel(const _Float16 *__rest
     *reinterpret_cast<half4 *>(o + b * o_b + (row - b * M) * o_i + 4 * c) = hv;
 }
 
-// Combine over many splits, plain graph: few rows (a long key range on a
+// Combine over many splits: few rows (a long key range on a
 // small batch) leave the one-thread-per-4-columns form with few workgroups,
 // each walking every split in turn. Here four groups of 64 threads share the
 // same rows: group g sums the g-th contiguous quarter of the splits in split
 // order, and group 0 then adds groups 1, 2, 3 in that order (fixed, so the
-// result is deterministic) before the division.
-template <int HD>
+// result is deterministic) before the division. With LSE every group first
+// takes the maximum lse over its quarter; the four maxima meet in LDS, so the
+// weights 2^(lse_s - max) use the same maximum as the one-group form.
+template <int HD, bool LSE>
 __global__ __launch_bounds__(256) void gqa_combine_grouped_kernel(const _Float16 *__restrict__ ws_o,
                                                                   const float *__restrict__ ws_l,
                                                                   _Float16 *__restrict__ o, long long o_b,
@@ -1137,18 +1139,28 @@ __global__ __launch_bounds__(256) void gqa_combine_grouped_kernel(const _Float16
     constexpr int CPR = HD / 4;    // threads per row, 4 head dims each
     constexpr int RPB = 64 / CPR;  // rows per workgroup
     __shared__ float red[3][5][64];
+    [[maybe_unused]] __shared__ float gmax[4][64];
     const int g = threadIdx.x >> 6, t = threadIdx.x & 63;
     const long long row = (long long)blockIdx.x * RPB + t / CPR;
     const int c = t % CPR;
     const bool valid = row < rows;
     const int s0 = g * nsplit / 4, s1 = (g + 1) * nsplit / 4;
+    [[maybe_unused]] float lmax = -__builtin_inff();
+    if constexpr (LSE) {
+        if (valid)
+            for (int s = s0; s < s1; ++s) lmax = __builtin_fmaxf(lmax, ws_l[(long long)s * rows + row]);
+        gmax[g][t] = lmax;
+        __syncthreads();
+        lmax = __builtin_fmaxf(__builtin_fmaxf(gmax[0][t], gmax[1][t]), __builtin_fmaxf(gmax[2][t], gmax[3][t]));
+    }
     float l = 0.f;
     float4v acc = {0.f, 0.f, 0.f, 0.f};
     if (valid) {
 #pragma unroll 8
         for (int s = s0; s < s1; ++s) {
             const long long prow = (long long)s * rows + row;
-            const float w = ws_l[prow];
+            float w = ws_l[prow];
+            if constexpr (LSE) w = w > -__builtin_inff() ? __builtin_amdgcn_exp2f(w - lmax) : 0.f;
             const half4 os = *reinterpret_cast<const half4 *>(ws_o + prow * HD + 4 * c);
             l += w;
 #pragma unroll
@@ -1284,15 +1296,21 @@ int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
     const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
     hipStream_t st = (hipStream_t)stream;
     _Float16 *oh = (_Float16 *)o;
-    if (!p.qknorm && p.splits >= kGroupedCombineSplits) {
+    if (p.splits >= kGroupedCombineSplits) {
         const long long rpb = 64 / (p.D / 4);
         const dim3 ggrid((unsigned)((rows + rpb - 1) / rpb));
-        if (p.D == 128)
-            hipLaunchKernelGGL((gqa_combine_grouped_kernel<128>), ggrid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
-                               p.st.o_i, p.M, rows, p.splits);
+        if (p.D == 128 && p.qknorm)
+            hipLaunchKernelGGL((gqa_combine_grouped_kernel<128, true>), ggrid, dim3(kThreads), 0, st, w, l, oh,
+                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
+        else if (p.D == 128)
+            hipLaunchKernelGGL((gqa_combine_grouped_kernel<128, false>), ggrid, dim3(kThreads), 0, st, w, l, oh,
+                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
+        else if (p.qknorm)
+            hipLaunchKernelGGL((gqa_combine_grouped_kernel<64, true>), ggrid, dim3(kThreads), 0, st, w, l, oh,
+                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
         else
-            hipLaunchKernelGGL((gqa_combine_grouped_kernel<64>), ggrid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
-                               p.st.o_i, p.M, rows, p.splits);
+            hipLaunchKernelGGL((gqa_combine_grouped_kernel<64, false>), ggrid, dim3(kThreads), 0, st, w, l, oh,
+                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
         return (int)hipGetLastError();
     }
     if (p.D == 128 && p.qknorm)

@@ -52,7 +52,7 @@ constexpr int kKeyBlock = 128;
 // D * N * 2 bytes stay below 2^31.
 constexpr int max_keys(int D) { return (1 << 30) / D - 1; }
 constexpr int kThreads = 256;
-// Split count from which the plain combine runs four split groups per
+// Split count from which the combine runs four split groups per
 // workgroup (gqa_combine_grouped_kernel, which needs kThreads == 256). Cold
 // A/B, us per forward: (2, 256, 32768) at 32 splits 16.10 -> 14.53; at 8
 // splits (2, 256, 4096) 7.54 -> 7.77 and (64, 8, 8192) 27.89 -> 28.26, at 16
