@@ -60,6 +60,9 @@ def parse_args():
     ap.add_argument("--qk-norm", action="store_true",
                     help="time the QK-normalised variant (rms_norm of Q rows and key vectors, "
                          "eps 1e-6) instead of the plain graph")
+    ap.add_argument("--sweep-splits", default="",
+                    help="comma-separated split counts: time the forward at each (same inputs, "
+                         "graph replay) and print one JSON line per count instead of the bench line")
     return ap.parse_args()
 
 
@@ -142,6 +145,22 @@ def gpu_clocks():
         except (OSError, ValueError):
             continue
     return out or None
+
+
+def read_load_clock(config: str):
+    """Shader clock under load (GHz) from the committed counter pass of this
+    workload: GRBM_GUI_ACTIVE per XCD over the dispatch's own duration, if that
+    pass was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_gqa_partial_{config.replace('gqa_', '')}.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"load_clock_ghz:\s*([0-9.]+)", text)
+    if not (sha and val) or sha.group(1) != kernel_source_sha():
+        return None
+    return float(val.group(1))
 
 
 def time_eager(torch, stream, fn, n_steps, warmup):
@@ -265,10 +284,46 @@ def main():
         if rc:
             raise mga.GqaError(rc)
 
+    gsteps = max(1, min(args.graph_steps, args.steps))
+    if args.sweep_splits:
+        # One JSON line per split count: the forward at that count, same
+        # rotating inputs, graph replay (the bench line's timing).
+        for sp in (int(x) for x in args.sweep_splits.split(",")):
+            eff_sp = mga.mga_gqa_effective_splits(B, M, N, D, sp)
+            if eff_sp < 0:
+                continue
+            ws_sp = mga.workspace_for(B, M, N, D, sp, device=dev)
+            wp, wb = (0, 0) if ws_sp is None else (ws_sp.data_ptr(), ws_sp.numel())
+
+            def fwd_sp(i, sp=sp, wp=wp, wb=wb):
+                j = i % R
+                rc = lib.mga_gqa_forward(*ptrs[j], optr[j], B, M, N, D, sp, wp, wb, sh)
+                if rc:
+                    raise mga.GqaError(rc)
+
+            def part_sp(i, sp=sp, wp=wp, wb=wb):
+                j = i % R
+                rc = lib.mga_gqa_partial(*ptrs[j], optr[j], B, M, N, D, sp, wp, wb, sh)
+                if rc:
+                    raise mga.GqaError(rc)
+
+            with torch.cuda.stream(stream):
+                ms_f, _, _ = time_graph(torch, stream, fwd_sp, args.steps, gsteps, args.warmup)
+                ms_p, _, _ = time_graph(torch, stream, part_sp, args.steps, gsteps, args.warmup)
+            rows = mga.mga_gqa_plan(B, M, N, D, sp)[1]
+            print(json.dumps({"workload": cfg.name, "requested_splits": sp, "splits": eff_sp,
+                              "tile_rows": rows, "us_per_forward": round(ms_f * 1e3, 3),
+                              "us_partial_kernel": round(ms_p * 1e3, 3),
+                              "frac_hbm_peak_forward": round(cfg.algorithmic_bytes / (ms_f * 1e-3)
+                                                             / (HBM_PEAK_GBPS * 1e9), 4),
+                              "rotating_sets": R, "steps": max(1, math.ceil(args.steps / gsteps)) * gsteps}),
+                  flush=True)
+            del ws_sp
+        return
+
     print(f"[bench] {cfg.name} B={B} M={M} N={N} D={D} splits={eff} rotating sets={R} "
           f"({R * set_bytes / 2**20:.0f} MiB) steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
-    gsteps = max(1, min(args.graph_steps, args.steps))
 
     def combine(i, rotate=True):
         j = i % R if rotate else 0
@@ -323,10 +378,16 @@ def main():
     t_hbm = alg_bytes / (HBM_PEAK_GBPS * 1e9)
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
     sp = ms_partial * 1e-3
+    # The partial kernel's own algorithmic bytes: Q, K and V read once, and O
+    # written once only when it runs unsplit (split, it leaves O to the combine).
+    kernel_bytes = alg_bytes - (0 if eff == 1 else B * M * D * 2)
     if bound == "hbm":
-        achieved, peak, unit = alg_bytes / sp / 1e9, HBM_PEAK_GBPS, "GB/s"
+        achieved, peak, unit = kernel_bytes / sp / 1e9, HBM_PEAK_GBPS, "GB/s"
+        achieved_f = alg_bytes / s / 1e9
     else:
         achieved, peak, unit = flops / sp / 1e12, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"
+        achieved_f = flops / s / 1e12
+    load_ghz = read_load_clock(cfg.name)
 
     result = {
         "metric": "fused GQA exp-sum-div attention TFLOP/s + HBM GB/s on 1 MI355X",
@@ -356,8 +417,21 @@ def main():
                      "frac": round(achieved / peak, 4),
                      "traffic": None if args.qk_norm else read_traffic(cfg.name),
                      "kernel": "gqa_partial_kernel + gqa_combine_kernel (QK norm)" if args.qk_norm
-                     else "gqa_partial_kernel"},
+                     else "gqa_partial_kernel",
+                     "scope": "the dominant kernel alone: its algorithmic bytes (Q, K, V read; O only "
+                              "when unsplit) over its graph-replayed launch time"},
+        "roofline_forward": {"bound": bound, "achieved": round(achieved_f, 2), "peak": peak, "unit": unit,
+                             "frac": round(achieved_f / peak, 4),
+                             "scope": "the whole forward (partial kernel + combine and the launch "
+                                      "boundaries between them): Q, K, V read, O written, over ms_per_step"},
     }
+    if load_ghz:
+        # MFMA roof at the shader clock measured under load (counter pass of
+        # the same kernel source), next to the nominal 2.4 GHz one.
+        peak_load = MFMA_FP16_PEAK_TFLOPS * load_ghz / 2.4
+        result["mfma_at_load_clock"] = {"clock_ghz": load_ghz, "peak_tflops": round(peak_load, 1),
+                                        "frac_forward": round(flops / s / 1e12 / peak_load, 4),
+                                        "frac_partial_kernel": round(flops / sp / 1e12 / peak_load, 4)}
     result["gpu_clocks"] = {"before": clocks_before, "after": clocks_after}
     if replays:
         result["replays"] = replays  # spread of the per-replay means within the timed steps

@@ -66,7 +66,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
 #include <type_traits>
+#include <utility>
 
 #include "mga_internal.h"
 
@@ -1206,6 +1208,21 @@ __global__ __launch_bounds__(256) void repack_k_kernel(const _Float16 *__restric
     *reinterpret_cast<half8 *>(dst + row * n8 + c) = out;
 }
 
+// Enqueues `kernel` on `stream` and returns the status of this launch alone
+// (hipLaunchKernel's own result), not an error an earlier HIP call of the
+// caller may have left pending.
+template <typename... P, typename... A>
+int launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A &&...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "argument count");
+    std::tuple<P...> vals(std::forward<A>(args)...);  // the kernel's own parameter types
+    void *ptrs[sizeof...(P)];
+    std::apply([&](auto &...v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void *>(&v)), ...);
+    }, vals);
+    return (int)hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+}
+
 template <int HD, int QT, int QW, int KS, bool KM, bool QKN>
 int launch_partial_layout(const mga::Plan &p, const _Float16 *q, const _Float16 *k, const _Float16 *v,
                           _Float16 *o, _Float16 *w, float *l, hipStream_t st) {
@@ -1214,9 +1231,8 @@ int launch_partial_layout(const mga::Plan &p, const _Float16 *q, const _Float16 
     const int pairs = p.B * p.splits;
     const int groups = (pairs + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.mtiles));
-    hipLaunchKernelGGL((gqa_partial_kernel<HD, QT, QW, KS, KM, QKN>), grid, dim3(64 * QW * KS), 0, st, q, k, v,
-                       o, w, l, p.st, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles, p.eps);
-    return (int)hipGetLastError();
+    return launch(gqa_partial_kernel<HD, QT, QW, KS, KM, QKN>, grid, dim3(64 * QW * KS), st, q, k, v, o, w, l,
+                  p.st, p.B, p.M, p.N, p.chunk_keys, p.splits, p.mtiles, p.eps);
 }
 
 template <int HD, int QT, int QW, int KS, bool QKN = false>
@@ -1282,9 +1298,8 @@ int launch_repack(const Plan &p, const void *k, void *ws, void *stream) {
     const long long rows = (long long)p.B * p.D;
     const long long threads = rows * (n8 / 8);
     const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(repack_k_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, (const _Float16 *)k,
-                       (_Float16 *)((char *)ws + p.repack_off), rows, p.N, n8);
-    return (int)hipGetLastError();
+    return launch(repack_k_kernel, grid, dim3(kThreads), (hipStream_t)stream, (const _Float16 *)k,
+                  (_Float16 *)((char *)ws + p.repack_off), rows, p.N, n8);
 }
 
 int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
@@ -1292,40 +1307,20 @@ int launch_combine(const Plan &p, void *o, const void *ws, void *stream) {
     float *l = nullptr;
     ws_split(p, ws, &w, &l);
     const long long rows = (long long)p.B * p.M;
-    const long long threads = rows * (p.D / 4);
-    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
     hipStream_t st = (hipStream_t)stream;
     _Float16 *oh = (_Float16 *)o;
     if (p.splits >= kGroupedCombineSplits) {
         const long long rpb = 64 / (p.D / 4);
         const dim3 ggrid((unsigned)((rows + rpb - 1) / rpb));
-        if (p.D == 128 && p.qknorm)
-            hipLaunchKernelGGL((gqa_combine_grouped_kernel<128, true>), ggrid, dim3(kThreads), 0, st, w, l, oh,
-                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
-        else if (p.D == 128)
-            hipLaunchKernelGGL((gqa_combine_grouped_kernel<128, false>), ggrid, dim3(kThreads), 0, st, w, l, oh,
-                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
-        else if (p.qknorm)
-            hipLaunchKernelGGL((gqa_combine_grouped_kernel<64, true>), ggrid, dim3(kThreads), 0, st, w, l, oh,
-                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
-        else
-            hipLaunchKernelGGL((gqa_combine_grouped_kernel<64, false>), ggrid, dim3(kThreads), 0, st, w, l, oh,
-                               p.st.o_b, p.st.o_i, p.M, rows, p.splits);
-        return (int)hipGetLastError();
+        auto kern = p.D == 128 ? (p.qknorm ? gqa_combine_grouped_kernel<128, true> : gqa_combine_grouped_kernel<128, false>)
+                               : (p.qknorm ? gqa_combine_grouped_kernel<64, true> : gqa_combine_grouped_kernel<64, false>);
+        return launch(kern, ggrid, dim3(kThreads), st, w, l, oh, p.st.o_b, p.st.o_i, p.M, rows, p.splits);
     }
-    if (p.D == 128 && p.qknorm)
-        hipLaunchKernelGGL((gqa_combine_kernel<128, true>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
-                           p.st.o_i, p.M, rows, p.splits);
-    else if (p.D == 128)
-        hipLaunchKernelGGL((gqa_combine_kernel<128, false>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
-                           p.st.o_i, p.M, rows, p.splits);
-    else if (p.qknorm)
-        hipLaunchKernelGGL((gqa_combine_kernel<64, true>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
-                           p.st.o_i, p.M, rows, p.splits);
-    else
-        hipLaunchKernelGGL((gqa_combine_kernel<64, false>), grid, dim3(kThreads), 0, st, w, l, oh, p.st.o_b,
-                           p.st.o_i, p.M, rows, p.splits);
-    return (int)hipGetLastError();
+    const long long threads = rows * (p.D / 4);
+    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    auto kern = p.D == 128 ? (p.qknorm ? gqa_combine_kernel<128, true> : gqa_combine_kernel<128, false>)
+                           : (p.qknorm ? gqa_combine_kernel<64, true> : gqa_combine_kernel<64, false>);
+    return launch(kern, grid, dim3(kThreads), st, w, l, oh, p.st.o_b, p.st.o_i, p.M, rows, p.splits);
 }
 
 }  // namespace mga

@@ -45,7 +45,11 @@
  * error. Results are deterministic for a fixed (shape, splits): every
  * sum runs in a fixed order and no atomics are used. Inputs whose scores reach
  * ln(65504) ~ 11.09 overflow fp16 P; results are then undefined (the graph
- * itself overflows there).
+ * itself overflows there). At the other end, a score below ln(2^-24) ~ -16.6
+ * gives P = 0 (fp16 flushes it): a row all of whose scores lie there has
+ * S = 0 and its output is 0/0 = NaN, as in the fp16 graph (the exact
+ * real-valued softmax would still be finite). Scores between -16.6 and
+ * ln(2^-14) ~ -9.7 land on fp16 subnormals.
  *
  * Ownership and asynchrony: the caller owns q, k, v, o and the workspace; the
  * library allocates and frees nothing on the device and keeps no device state,
@@ -55,7 +59,9 @@
  *
  * Errors: every entry point validates its arguments on the host before any
  * launch and returns an mga_status; on a nonzero status nothing was launched,
- * except MGA_ERR_HIP, which reports a failed launch (hipGetLastError).
+ * except MGA_ERR_HIP, which reports a launch the runtime refused: the status
+ * hipLaunchKernel returned for that launch, not an error that an earlier HIP
+ * call of the caller left for hipGetLastError.
  */
 #ifndef MGA_GQA_H
 #define MGA_GQA_H
@@ -87,7 +93,9 @@ typedef enum {
 #define MGA_HEAD_DIM 64
 #define MGA_HEAD_DIM_WIDE 128
 
-/* Human-readable text for a status code (static storage, never NULL). */
+/* Human-readable text for a status code (static storage, never NULL). The
+ * codes follow the transpiler error codes of the kaispace blog, section 5.1
+ * (success 0, insufficient shared memory 1, layout error 2, config error 3). */
 const char *mga_status_string(int status);
 
 /* Split policy (host only, deterministic): the number of KV splits the
@@ -97,13 +105,17 @@ const char *mga_status_string(int status);
  * rule picks it instead of a search. */
 int mga_gqa_choose_splits(int B, int M, int N, int D);
 
-/* The split count actually launched for a requested `splits` (0 = policy):
+/* The split count actually launched for a requested `splits` (0 = policy);
+ * the grid dimension and for-loop range of the kaispace blog, section 4.2:
  * the chunk is ceil(ceil(N/128) / splits) key blocks and the count is
  * ceil(ceil(N/128) / chunk), so that no split is empty. Returns -1 for
  * arguments mga_gqa_check_args would reject with INVALID_VALUE or CONFIG. */
 int mga_gqa_effective_splits(int B, int M, int N, int D, int splits);
 
-/* Bytes of workspace mga_gqa_forward needs: with an effective split count
+/* Bytes of workspace mga_gqa_forward needs. It plays the role of the runtime
+ * buffer `buf` that the generated host entry receives (Mirage documentation,
+ * "Generated CUDA Code Example") and whose size the CUDA transpiler reports
+ * (kaispace blog, section 5.2). With an effective split count
  * s > 1, the normalised partials o[s][B][M][D] in fp16 (s*B*M*D*2 bytes,
  * rounded up to 256) followed by the denominators L[s][B][M] in fp32
  * (s*B*M*4 bytes), rounded up to 256; then, when N % 8 != 0, the copy of K
@@ -114,7 +126,9 @@ int mga_gqa_effective_splits(int B, int M, int N, int D, int splits);
 size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
 
 /* The launch geometry the library picks (host only): query rows per
- * workgroup and the effective split count. D = 64: 256 or 128 rows when that
+ * workgroup and the effective split count, i.e. the block-grid shape and the
+ * for-loop range that the kaispace blog (section 4.2) lists as search
+ * parameters, chosen here by a fixed rule. D = 64: 256 or 128 rows when that
  * tile alone gives at least 256 workgroups (one per compute unit), else 256
  * rows when two splits do, else 64 rows, or 32 rows when even the most splits
  * leave 64-row tiles short of 256 workgroups (and always for M <= 32);
@@ -125,15 +139,20 @@ size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
  * memory layout is not part of the plan. */
 int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
 
-/* Host-only validation of a forward call; makes no HIP call and launches
- * nothing, so it is usable without a GPU. Returns the status
+/* Host-only validation of a forward call, the counterpart of compile()'s
+ * check that run-time tensors match the graph's shapes and strides (kaispace
+ * blog, section 2); makes no HIP call and launches nothing, so it is usable
+ * without a GPU. Returns the status
  * mga_gqa_forward would return before launching. `ws` may be NULL when the
  * effective split count is 1. B == 0 or M == 0 is valid (a no-op). */
 int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o,
                        int B, int M, int N, int D, int splits, const void *ws, size_t ws_bytes);
 
-/* The whole path: partial kernel, then (when the effective split count is
- * above 1) the combine kernel, both on `stream`. splits = 0 lets the policy
+/* The whole path (the graph of the Mirage documentation page "Mirage: Define
+ * GQA Computation Graph", evaluated as the for-loop-accumulate plus combine
+ * form of the kaispace blog, sections 2.1 and 4.2-4.3): partial kernel, then
+ * (when the effective split count is above 1) the combine kernel, both on
+ * `stream`. splits = 0 lets the policy
  * choose. ws/ws_bytes: caller-owned device workspace of at least
  * mga_gqa_workspace_bytes(B, M, N, D, splits) bytes, 16-byte aligned. Calls
  * that share a workspace must not overlap in time. */
@@ -142,7 +161,7 @@ int mga_gqa_forward(const void *q, const void *k, const void *v, void *o,
                     void *stream);
 
 /* mga_gqa_forward on strided views: graph inputs declared with other strides
- * (the same blog section: new_input accepts explicit strides), e.g. K as the
+ * (kaispace blog, section 2: new_input accepts explicit strides), e.g. K as the
  * transpose of a [keys][head dim] cache, or K and V interleaved in one cache. `strides` points to nine element strides
  * (not bytes), in this order:
  *     q_b, q_i          Q[b][i][d] at q + b*q_b + i*q_i + d
@@ -165,13 +184,15 @@ int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o
                             int B, int M, int N, int D, const int64_t *strides, int splits,
                             void *ws, size_t ws_bytes, void *stream);
 
-/* Host-only validation of a mga_gqa_forward_strided call (no HIP call). */
+/* Host-only validation of a mga_gqa_forward_strided call (no HIP call); the
+ * shape and stride check of compile() (kaispace blog, section 2). */
 int mga_gqa_check_args_strided(const void *q, const void *k, const void *v, const void *o,
                                int B, int M, int N, int D, const int64_t *strides, int splits,
                                const void *ws, size_t ws_bytes);
 
-/* Only the split-KV partial kernel (the for-loop over keys; preceded by the
- * K copy when N % 8 != 0). With one effective split it writes O directly
+/* Only the split-KV partial kernel (the for-loop over keys with
+ * accumulation, kaispace blog sections 2.1 and 4.2: forloop_dim / fmap over
+ * the key dimension; preceded by the K copy when N % 8 != 0). With one effective split it writes O directly
  * (normalised, fp16); otherwise it writes the normalised partials and
  * denominators into `ws` and leaves `o` untouched. Same arguments and checks
  * as mga_gqa_forward. */
@@ -179,7 +200,9 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
                     int B, int M, int N, int D, int splits, void *ws, size_t ws_bytes,
                     void *stream);
 
-/* Only the combine kernel:
+/* Only the combine kernel (the second block graph that sums the grid blocks'
+ * partial results, kaispace blog sections 2.1 and 4.5, partial_sum /
+ * combine):
  *     O[b,i,:] = fp16(sum_s L[s,b,i] o[s,b,i,:] / sum_s L[s,b,i])
  * with the sums taken in fp32 in a fixed order (split order; from 32 splits,
  * four contiguous quarters in split order, then the quarters in order). `ws` holds the partials a preceding
@@ -212,15 +235,16 @@ int mga_gqa_qknorm_forward(const void *q, const void *k, const void *v, void *o,
                            int splits, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes mga_gqa_qknorm_forward needs (same form as
- * mga_gqa_workspace_bytes, for this path's split count); 0 for invalid
- * shapes or one split. */
+ * mga_gqa_workspace_bytes, for this path's split count; the runtime buffer of
+ * the kaispace blog, section 5.2); 0 for invalid shapes or one split. */
 size_t mga_gqa_qknorm_workspace_bytes(int B, int M, int N, int D, int splits);
 
 /* Tile rows and effective split count of the QK-normalised path (as
- * mga_gqa_plan). */
+ * mga_gqa_plan; kaispace blog, section 4.2). */
 int mga_gqa_qknorm_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
 
-/* Host-only validation of a mga_gqa_qknorm_forward call (no HIP call). */
+/* Host-only validation of a mga_gqa_qknorm_forward call (no HIP call; the
+ * compile()-time shape and stride check, kaispace blog section 2). */
 int mga_gqa_qknorm_check_args(const void *q, const void *k, const void *v, const void *o,
                               int B, int M, int N, int D, float eps, const int64_t *strides,
                               int splits, const void *ws, size_t ws_bytes);

@@ -27,6 +27,24 @@ def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(_lib.SIGNATURES)
 
 
+CITATION = re.compile(r"kaispace blog|Mirage documentation|Mirage docs")
+
+
+def test_every_declaration_cites_its_passage():
+    """The comment block in front of each declaration (the text since the
+    previous declaration) names the page passage that defines the call."""
+    text = open(HEADER).read()
+    body = text[text.index("extern \"C\" {"):]
+    starts = [(m.start(), m.group(1)) for m in re.finditer(r"^[a-z][\w\s\*]*\b(mga_\w+)\s*\(", body, re.M)]
+    assert sorted(n for _, n in starts) == sorted(_lib.SIGNATURES)
+    prev = 0
+    for pos, name in starts:
+        comments = " ".join(re.findall(r"/\*.*?\*/", body[prev:pos], flags=re.S))
+        comments = re.sub(r"\s*\n\s*\*?\s*", " ", comments)  # join wrapped comment lines
+        assert CITATION.search(comments), f"{name}: no passage cited in the comment before it"
+        prev = body.index(";", pos) + 1
+
+
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in header_functions():

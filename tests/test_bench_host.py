@@ -67,3 +67,15 @@ def test_oracle_thread_count_changes_no_result():
         oracle.set_threads(n_all)
     assert oracle.threads() == n_all
     assert np.array_equal(a, b)
+
+
+def test_load_clock_only_from_the_current_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    d = tmp_path / "profiles"
+    d.mkdir()
+    f = d / "counters_gqa_partial_b16_m256_n4096.md"
+    f.write_text(f"kernel_source_sha256: {bench.kernel_source_sha()}\nload_clock_ghz: 2.05\n")
+    assert bench.read_load_clock("gqa_b16_m256_n4096") == 2.05
+    f.write_text("kernel_source_sha256: " + "0" * 64 + "\nload_clock_ghz: 2.05\n")
+    assert bench.read_load_clock("gqa_b16_m256_n4096") is None
+    assert bench.read_load_clock("gqa_b64_m8_n8192") is None

@@ -7,7 +7,8 @@ captured once and replayed several times with eager work of the program
 Every replay must reproduce the eager outputs bit for bit: the kernels are
 deterministic for a fixed shape and split count, and the path records no
 memset node. Covers split and unsplit shapes, both ring disciplines, the K
-repack (N % 8 != 0) and the QK-normalised variant.
+repack (N % 8 != 0), the QK-normalised variant and the grouped combine
+(32 splits and more).
 """
 import numpy as np
 import pytest
@@ -24,6 +25,8 @@ CASES = [
     (3, 8, 3000, 64, 0, False),      # decode rows: 32-row private ring
     (8, 1, 1032, 128, 0, False),     # head dim 128
     (2, 64, 1032, 64, 0, True),      # QK-normalised
+    (2, 256, 32768, 64, 0, False),   # long keys: 32 splits, the grouped combine
+    (2, 256, 32768, 64, 0, True),    # the same through the QK-normalised (lse) grouped combine
 ]
 
 

@@ -90,7 +90,8 @@ def test_qknorm_small_and_ragged(gpu, B, M, N, D):
 
 
 @pytest.mark.parametrize("name,rows", [("gqa_b16_m256_n4096", 16), ("gqa_b64_m1_n4096_d128", 1),
-                                       ("gqa_b64_m8_n8192", 8)])
+                                       ("gqa_b64_m8_n8192", 8), ("gqa_b2_m256_n32768", 24),
+                                       ("gqa_b128_m256_n16384", 2)])
 def test_qknorm_full_size_sampled_rows(gpu, name, rows):
     cfg = CONFIGS[name]
     q, k, v = make_config(cfg)
