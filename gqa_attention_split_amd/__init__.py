@@ -25,6 +25,8 @@ MGA_ERR_LAYOUT = 2
 MGA_ERR_CONFIG = 3
 MGA_ERR_WORKSPACE = 4
 MGA_ERR_HIP = 5
+MGA_ERR_SCRATCH = 6
+NOALLOC_SCRATCH_BYTES = 16 << 20
 KEY_BLOCK = 128
 HEAD_DIMS = (64, 128)
 
@@ -100,6 +102,11 @@ def mga_gqa_forward_strided(q, k, v, o, B, M, N, D, strides, splits, ws, ws_byte
     return _lib.load().mga_gqa_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D,
                                                _strides(strides), splits, _ptr(ws), ws_bytes,
                                                _stream(stream))
+
+
+def mga_gqa_forward_noalloc(q, k, v, o, B, M, N, D, strides, splits, stream) -> int:
+    return _lib.load().mga_gqa_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, M, N, D,
+                                               _strides(strides), splits, _stream(stream))
 
 
 def mga_gqa_check_args_strided(q, k, v, o, B, M, N, D, strides, splits, ws, ws_bytes) -> int:

@@ -28,6 +28,7 @@ SIGNATURES = {
     "mga_gqa_combine": ([_P, _I, _I, _I, _I, _I, _P, _S, _P], _I),
     "mga_gqa_forward_strided": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _S, _P], _I),
     "mga_gqa_check_args_strided": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _S], _I),
+    "mga_gqa_forward_noalloc": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "mga_gqa_qknorm_forward": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _P, _S, _P], _I),
     "mga_gqa_qknorm_workspace_bytes": ([_I, _I, _I, _I, _I], _S),
     "mga_gqa_qknorm_plan": ([_I, _I, _I, _I, _I, _P, _P], _I),

@@ -66,6 +66,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -1244,7 +1245,34 @@ int launch_partial_cfg(const mga::Plan &p, const _Float16 *q, const _Float16 *k,
 
 }  // namespace
 
+// Library-owned device scratch of mga_gqa_forward_noalloc (the workspace of
+// callers that cannot allocate): kScratchBytes per GPU, allocated with the
+// code object when the library is first used on that GPU and held until the
+// process ends. Host code never names it directly: scratch_ptr returns the
+// address the runtime reports for the current device.
+static __device__ __align__(256) char scratch[mga::kScratchBytes];
+
 namespace mga {
+
+int scratch_ptr(void **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *per_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));  // with `dev` current
+        if (e != hipSuccess) return (int)e;
+        if (!ptr) return (int)hipErrorInvalidSymbol;
+        per_device[dev] = ptr;
+    }
+    *out = per_device[dev];
+    return 0;
+}
 
 // Workspace: o_s [splits][B][M][D] fp16, then (from a 256-byte boundary)
 // L_s [splits][B][M] fp32.

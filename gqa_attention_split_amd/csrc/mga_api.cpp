@@ -206,6 +206,9 @@ const char *mga_status_string(int status) {
                "a stride or byte extent too large, or a grid too large";
     case MGA_ERR_WORKSPACE: return "MGA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MGA_ERR_HIP: return "MGA_ERR_HIP: kernel launch failed";
+    case MGA_ERR_SCRATCH:
+        return "MGA_ERR_SCRATCH: the call needs more workspace than the 16 MiB device scratch of "
+               "mga_gqa_forward_noalloc holds";
     default: return "unknown mga status";
     }
 }
@@ -276,6 +279,20 @@ int mga_gqa_forward(const void *q, const void *k, const void *v, void *o, int B,
     return mga_gqa_forward_strided(q, k, v, o, B, M, N, D, nullptr, splits, ws, ws_bytes, stream);
 }
 
+// The launches of one checked forward: K repack (if planned), partial
+// kernel, combine (split plans), in that order on `stream`.
+static int run_forward(const mga::Plan &p, const void *q, const void *k, const void *v, void *o, void *ws,
+                       void *stream) {
+    if (p.B == 0 || p.M == 0) return MGA_OK;
+    if (p.repack) {
+        if (mga::launch_repack(p, k, ws, stream) != 0) return MGA_ERR_HIP;
+        k = (const char *)ws + p.repack_off;
+    }
+    if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
+    if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
+    return MGA_OK;
+}
+
 int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o, int B, int M,
                             int N, int D, const int64_t *strides, int splits, void *ws,
                             size_t ws_bytes, void *stream) {
@@ -284,14 +301,22 @@ int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o
     if (rc == MGA_OK) rc = mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
     if (rc == MGA_OK) rc = mga::check_call(q, k, v, o, p, ws, ws_bytes, true);
     if (rc != MGA_OK) return rc;
-    if (B == 0 || M == 0) return MGA_OK;
-    if (p.repack) {
-        if (mga::launch_repack(p, k, ws, stream) != 0) return MGA_ERR_HIP;
-        k = (const char *)ws + p.repack_off;
-    }
-    if (mga::launch_partial(p, q, k, v, o, ws, stream) != 0) return MGA_ERR_HIP;
-    if (p.splits > 1 && mga::launch_combine(p, o, ws, stream) != 0) return MGA_ERR_HIP;
-    return MGA_OK;
+    return run_forward(p, q, k, v, o, ws, stream);
+}
+
+int mga_gqa_forward_noalloc(const void *q, const void *k, const void *v, void *o, int B, int M,
+                            int N, int D, const int64_t *strides, int splits, void *stream) {
+    static_assert(mga::kScratchBytes == (size_t)MGA_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+    mga::Plan p;
+    int rc = mga::make_plan(B, M, N, D, splits, &p);
+    if (rc == MGA_OK) rc = mga::set_layout(&p, reinterpret_cast<const long long *>(strides));
+    if (rc != MGA_OK) return rc;
+    if (p.ws_bytes > mga::kScratchBytes) return MGA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0 && p.B > 0 && p.M > 0 && mga::scratch_ptr(&ws) != 0) return MGA_ERR_HIP;
+    rc = mga::check_call(q, k, v, o, p, ws, mga::kScratchBytes, true);
+    if (rc != MGA_OK) return rc;
+    return run_forward(p, q, k, v, o, ws, stream);
 }
 
 int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits) {

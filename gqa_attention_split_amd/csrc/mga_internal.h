@@ -76,6 +76,12 @@ int set_layout(Plan *p, const long long *strides);
 int check_call(const void *q, const void *k, const void *v, const void *o, const Plan &p,
                const void *ws, size_t ws_bytes, bool need_inputs);
 
+// Bytes of the fixed device scratch behind mga_gqa_forward_noalloc.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+// Address of that scratch on the current device (looked up once per device);
+// 0 or a hipError_t value.
+int scratch_ptr(void **out);
+
 // Kernel launchers (gqa_kernels.hip). Return 0 or a hipError_t value.
 int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,
                    void *ws, void *stream);

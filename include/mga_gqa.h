@@ -84,7 +84,8 @@ typedef enum {
     MGA_ERR_CONFIG = 3,        /* D not 64/128, splits > ceil(N / 128), N > 2^30/D - 1,
                                   grid too big                                      */
     MGA_ERR_WORKSPACE = 4,     /* workspace missing, misaligned or too small        */
-    MGA_ERR_HIP = 5            /* a kernel launch failed                            */
+    MGA_ERR_HIP = 5,           /* a kernel launch failed                            */
+    MGA_ERR_SCRATCH = 6        /* mga_gqa_forward_noalloc: workspace above its scratch */
 } mga_status;
 
 /* Keys per pipeline stage; split chunks are whole multiples of it. */
@@ -210,6 +211,25 @@ int mga_gqa_partial(const void *q, const void *k, const void *v, void *o,
  * not read. A no-op returning MGA_OK when the effective split count is 1. */
 int mga_gqa_combine(void *o, int B, int M, int N, int D, int splits,
                     const void *ws, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and arguments as mga_gqa_forward_strided (strides NULL =
+ * contiguous; splits 0 = policy), with no workspace argument. The workspace
+ * the plan needs (mga_gqa_workspace_bytes) comes from one device scratch
+ * array of MGA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU that the library owns:
+ * it is part of the library's code object, so it exists from the library's
+ * first use on that GPU until the process ends, and this call allocates and
+ * frees nothing (its address is looked up once per device, on the first
+ * call with that device current). A plan that needs more than the scratch
+ * returns MGA_ERR_SCRATCH and launches nothing. Every call on one GPU shares
+ * that GPU's scratch, which keeps the last call's contents (nothing in it
+ * needs clearing): calls that overlap in time on one GPU race and give
+ * undefined results, so the caller serialises them (e.g. one stream). */
+#define MGA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mga_gqa_forward_noalloc(const void *q, const void *k, const void *v, void *o,
+                            int B, int M, int N, int D, const int64_t *strides, int splits,
+                            void *stream);
 
 /* ---- QK-normalised variant ---------------------------------------------
  * Attention with QK normalisation (Mirage documentation tutorial "Implement

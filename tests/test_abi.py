@@ -28,6 +28,8 @@ def test_header_declares_the_documented_entry_points():
 
 
 CITATION = re.compile(r"kaispace blog|Mirage documentation|Mirage docs")
+# The one entry point outside the pages' passages names the callers it serves.
+NO_ALLOC_CALLERS = re.compile(r"callers that cannot allocate")
 
 
 def test_every_declaration_cites_its_passage():
@@ -41,7 +43,8 @@ def test_every_declaration_cites_its_passage():
     for pos, name in starts:
         comments = " ".join(re.findall(r"/\*.*?\*/", body[prev:pos], flags=re.S))
         comments = re.sub(r"\s*\n\s*\*?\s*", " ", comments)  # join wrapped comment lines
-        assert CITATION.search(comments), f"{name}: no passage cited in the comment before it"
+        want = NO_ALLOC_CALLERS if name == "mga_gqa_forward_noalloc" else CITATION
+        assert want.search(comments), f"{name}: no passage cited in the comment before it"
         prev = body.index(";", pos) + 1
 
 
@@ -57,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         s = mga.mga_status_string(code)
         assert s.startswith("MGA_"), s
     assert "unknown" in mga.mga_status_string(99)
@@ -295,3 +298,15 @@ def test_repack_workspace_for_unaligned_contiguous_k():
             assert mga.mga_gqa_workspace_bytes(B, M, N, D, splits) == part + -(-B * D * n8 * 2 // 256) * 256
             assert mga.mga_gqa_check_args(A, A, A, A, B, M, N, D, splits, A,
                                           mga.mga_gqa_workspace_bytes(B, M, N, D, splits)) == mga.MGA_OK
+
+
+def test_noalloc_refuses_plans_above_its_scratch_without_a_gpu():
+    """The size check comes before any HIP call: a plan whose workspace is
+    larger than the fixed scratch (here the K copy of a contiguous K with
+    N % 8 != 0: 64*64*4104*2 bytes) is refused, as are invalid shapes."""
+    need = mga.mga_gqa_workspace_bytes(64, 256, 4100, 64, 0)
+    assert need > mga.NOALLOC_SCRATCH_BYTES
+    assert mga.mga_gqa_forward_noalloc(A, A, A, A, 64, 256, 4100, 64, None, 0, None) == mga.MGA_ERR_SCRATCH
+    assert mga.mga_gqa_forward_noalloc(A, A, A, A, 2, 256, 0, 64, None, 0, None) == mga.MGA_ERR_INVALID_VALUE
+    assert mga.mga_gqa_forward_noalloc(A, A, A, A, 2, 256, 4096, 96, None, 0, None) == mga.MGA_ERR_CONFIG
+    assert "16 MiB" in mga.mga_status_string(mga.MGA_ERR_SCRATCH)
