@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmga_gqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "gqa_kernels.hip"), os.path.join(CSRC, "mga_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gqa_kernels.hip"), os.path.join(CSRC, "mga_api.cpp"),
+           os.path.join(CSRC, "mga_device.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are turned off for every device compile.

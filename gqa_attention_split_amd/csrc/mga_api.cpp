@@ -21,8 +21,6 @@ namespace mga {
 
 namespace {
 
-constexpr int kCUs = 256;  // MI355X compute units; one 8-wave workgroup fills one
-
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 constexpr long long kMinChunkBlocks = 4;
@@ -40,9 +38,10 @@ int rows_for(int variant) {
     }
 }
 
-// Query rows per workgroup. The rule comes from cold-input tile x split
-// sweeps of the five benchmark shapes on MI355X:
-//   * a tile shape that fills the chip (256 workgroups) without splitting
+// Query rows per workgroup, for a chip of `cus` compute units (one 8-wave
+// workgroup fills one). The rule comes from cold-input tile x split sweeps of
+// the five benchmark shapes on MI355X (256 compute units):
+//   * a tile shape that fills the chip (a workgroup per CU) without splitting
 //     beats any split configuration: 256 rows, else 128 rows;
 //   * else 256-row tiles if two splits fill the chip;
 //   * else 64-row tiles with key splits, unless even the most splits the key
@@ -52,15 +51,15 @@ int rows_for(int variant) {
 //     workgroup.)
 // Rows M <= 32 take 32-row tiles. The QK-normalised path has only the 32-
 // and 64-row shapes (the 64-row one on the shared ring once keys are split).
-int variant_for(int B, int M, int N, int D, bool qknorm) {
+int variant_for(int B, int M, int N, int D, bool qknorm, long long cus) {
     if (D == 128) return kVariantDecode128;
     if (qknorm) return M <= 32 ? kVariantDecode : kVariantSmall;  // 32 or 64 rows
     if (M <= 32) return kVariantDecode;
     const long long b = B, ms = max_splits(N);
-    if (M > 128 && b * ceil_div(M, 256) >= kCUs) return kVariantLarge;
-    if (M > 64 && b * ceil_div(M, 128) >= kCUs) return kVariantMedium;
-    if (M > 128 && b * ceil_div(M, 256) * std::min(2LL, ms) >= kCUs) return kVariantLarge;
-    if (b * ceil_div(M, 64) * ms >= kCUs) return kVariantSmall;
+    if (M > 128 && b * ceil_div(M, 256) >= cus) return kVariantLarge;
+    if (M > 64 && b * ceil_div(M, 128) >= cus) return kVariantMedium;
+    if (M > 128 && b * ceil_div(M, 256) * std::min(2LL, ms) >= cus) return kVariantLarge;
+    if (b * ceil_div(M, 64) * ms >= cus) return kVariantSmall;
     return kVariantDecode;
 }
 
@@ -73,10 +72,10 @@ long long wgs_per_cu(int variant) { return variant == kVariantDecode ? 2 : 1; }
 // (one or two workgroups each), keeping at least kMinChunkBlocks key blocks
 // per split where N allows (shorter chunks cost more in partial traffic and
 // combine work than the extra workgroups gain).
-int policy_splits(int B, int M, int N, int variant) {
+int policy_splits(int B, int M, int N, int variant, long long cus) {
     if (N < 1 || B < 1 || M < 1) return 1;
     const long long base = (long long)B * ceil_div(M, rows_for(variant));
-    const long long s = std::min(ceil_div(kCUs * wgs_per_cu(variant), base), max_splits(N));
+    const long long s = std::min(ceil_div(cus * wgs_per_cu(variant), base), max_splits(N));
     return (int)std::max(1LL, s);
 }
 
@@ -93,7 +92,8 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     p->M = M;
     p->N = N;
     p->D = D;
-    p->variant = variant_for(B, M, N, D, qknorm);
+    const long long cus = device_cus();
+    p->variant = variant_for(B, M, N, D, qknorm, cus);
     p->qknorm = qknorm;
     p->eps = 0.f;
     p->repack = false;
@@ -103,7 +103,7 @@ int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm) {
     p->nblocks = (int)nblocks;
     p->key_major = false;
     p->st = Strides{(long long)M * D, (long long)D * N, (long long)N * D, (long long)M * D, D, N, D, D};
-    const int want = splits == 0 ? policy_splits(B, M, N, p->variant) : splits;
+    const int want = splits == 0 ? policy_splits(B, M, N, p->variant, cus) : splits;
     const long long chunk_blocks = ceil_div(nblocks, want);
     p->splits = (int)ceil_div(nblocks, chunk_blocks);
     p->chunk_keys = (int)(chunk_blocks * kKeyBlock);

@@ -61,7 +61,8 @@ constexpr int kThreads = 256;
 constexpr int kGroupedCombineSplits = 32;
 static_assert(kThreads == 256, "grouped combine: four groups of 64 threads");
 
-// Fills `p` for a call; returns an mga_status (0 = ok). Host only, no HIP calls.
+// Fills `p` for a call; returns an mga_status (0 = ok). Host only; its one
+// runtime query is device_cus() (the chip size the split policy fills).
 // The layout is left contiguous and unchecked; set_layout fixes it. With
 // qknorm the kernel shape comes from the wave-private-ring shapes only.
 int make_plan(int B, int M, int N, int D, int splits, Plan *p, bool qknorm = false);
@@ -81,6 +82,13 @@ constexpr size_t kScratchBytes = (size_t)16 << 20;
 // Address of that scratch on the current device (looked up once per device);
 // 0 or a hipError_t value.
 int scratch_ptr(void **out);
+
+// Compute units of the current device (mga_device.cpp; looked up once per
+// device); the split policy sizes the grid to them. kDefaultCUs (MI355X in
+// its default single-partition mode) when no device answers, e.g. on a host
+// without a GPU.
+constexpr int kDefaultCUs = 256;
+int device_cus();
 
 // Kernel launchers (gqa_kernels.hip). Return 0 or a hipError_t value.
 int launch_partial(const Plan &p, const void *q, const void *k, const void *v, void *o,

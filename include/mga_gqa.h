@@ -99,8 +99,19 @@ typedef enum {
  * (success 0, insufficient shared memory 1, layout error 2, config error 3). */
 const char *mga_status_string(int status);
 
-/* Split policy (host only, deterministic): the number of KV splits the
- * library uses for this shape when the caller passes splits = 0. Always in
+/* Chip size. The split policy fills the compute units of the calling
+ * thread's current HIP device: the planning calls (this one, and every call
+ * that sizes a workspace, plans or validates) ask the runtime once per device
+ * for its compute-unit count (hipDeviceAttributeMultiprocessorCount: 256 on
+ * MI355X in its default single-partition mode) and assume 256 when no device
+ * answers, e.g. on a host without a GPU. Beyond that query they make no HIP
+ * call, launch nothing and allocate nothing. Plan, size and launch with the
+ * same device current: split counts and workspace sizes can differ between
+ * devices of different sizes.
+ *
+ * Split policy (host only, deterministic for a given chip size): the number
+ * of KV splits the library uses for this shape when the caller passes
+ * splits = 0. Always in
  * [1, ceil(N / 128)]; returns 1 for N < 1. Following the kaispace blog
  * (section 4.2), the split count is a grid-dimension choice; here a fixed
  * rule picks it instead of a search. */
@@ -129,12 +140,13 @@ size_t mga_gqa_workspace_bytes(int B, int M, int N, int D, int splits);
 /* The launch geometry the library picks (host only): query rows per
  * workgroup and the effective split count, i.e. the block-grid shape and the
  * for-loop range that the kaispace blog (section 4.2) lists as search
- * parameters, chosen here by a fixed rule. D = 64: 256 or 128 rows when that
- * tile alone gives at least 256 workgroups (one per compute unit), else 256
- * rows when two splits do, else 64 rows, or 32 rows when even the most splits
- * leave 64-row tiles short of 256 workgroups (and always for M <= 32);
- * D = 128: 32 rows. Splits then bring the grid to 256 workgroups (512 for
- * 32-row tiles at D = 64, two of which share a compute unit), each keeping
+ * parameters, chosen here by a fixed rule. With C the compute units of the current
+ * device (256 on MI355X; see "Chip size" above): D = 64: 256 or 128 rows
+ * when that tile alone gives at least C workgroups (one per compute unit),
+ * else 256 rows when two splits do, else 64 rows, or 32 rows when even the
+ * most splits leave 64-row tiles short of C workgroups (and always for
+ * M <= 32); D = 128: 32 rows. Splits then bring the grid to C workgroups (2C
+ * for 32-row tiles at D = 64, two of which share a compute unit), each keeping
  * at least 4 blocks of 128 keys. Either output pointer
  * may be NULL. Returns MGA_OK, INVALID_VALUE or CONFIG for the shape; the
  * memory layout is not part of the plan. */
@@ -142,8 +154,8 @@ int mga_gqa_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *ef
 
 /* Host-only validation of a forward call, the counterpart of compile()'s
  * check that run-time tensors match the graph's shapes and strides (kaispace
- * blog, section 2); makes no HIP call and launches nothing, so it is usable
- * without a GPU. Returns the status
+ * blog, section 2); launches nothing (its one runtime query is the chip size,
+ * see "Chip size" above), so it is usable without a GPU. Returns the status
  * mga_gqa_forward would return before launching. `ws` may be NULL when the
  * effective split count is 1. B == 0 or M == 0 is valid (a no-op). */
 int mga_gqa_check_args(const void *q, const void *k, const void *v, const void *o,
@@ -185,8 +197,9 @@ int mga_gqa_forward_strided(const void *q, const void *k, const void *v, void *o
                             int B, int M, int N, int D, const int64_t *strides, int splits,
                             void *ws, size_t ws_bytes, void *stream);
 
-/* Host-only validation of a mga_gqa_forward_strided call (no HIP call); the
- * shape and stride check of compile() (kaispace blog, section 2). */
+/* Host-only validation of a mga_gqa_forward_strided call (launches
+ * nothing); the shape and stride check of compile() (kaispace blog,
+ * section 2). */
 int mga_gqa_check_args_strided(const void *q, const void *k, const void *v, const void *o,
                                int B, int M, int N, int D, const int64_t *strides, int splits,
                                const void *ws, size_t ws_bytes);
@@ -263,8 +276,8 @@ size_t mga_gqa_qknorm_workspace_bytes(int B, int M, int N, int D, int splits);
  * mga_gqa_plan; kaispace blog, section 4.2). */
 int mga_gqa_qknorm_plan(int B, int M, int N, int D, int splits, int *tile_rows, int *eff_splits);
 
-/* Host-only validation of a mga_gqa_qknorm_forward call (no HIP call; the
- * compile()-time shape and stride check, kaispace blog section 2). */
+/* Host-only validation of a mga_gqa_qknorm_forward call (launches nothing;
+ * the compile()-time shape and stride check, kaispace blog section 2). */
 int mga_gqa_qknorm_check_args(const void *q, const void *k, const void *v, const void *o,
                               int B, int M, int N, int D, float eps, const int64_t *strides,
                               int splits, const void *ws, size_t ws_bytes);
