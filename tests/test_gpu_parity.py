@@ -298,3 +298,28 @@ def test_gpu_rejects_misaligned_pointer_without_launching(gpu):
     rc = mga.mga_gqa_forward(buf.data_ptr() + 2, k, v, o, 1, 8, 8, 64, 0, None, 0,
                              torch.cuda.current_stream())
     assert rc == mga.MGA_ERR_LAYOUT
+
+
+@pytest.mark.parametrize("D,splits", [(64, 1), (64, 4), (128, 1), (128, 3)])
+def test_row_whose_weights_all_underflow_is_nan(gpu, D, splits):
+    """The documented underflow case: a row whose every score is below
+    ln(2^-24) has P = fp16(e^a) = 0 for every key, so L = 0 and the output is
+    0/0 = NaN, as the fp16 graph gives (the fp64 oracle, whose exp does not
+    underflow there, returns a finite softmax). Every other row stays within
+    the contract tolerance, including the rest of that batch (constant K:
+    equal scores, the mean of V)."""
+    B, M, N = 2, 40, 520
+    q, k, v = make_qkv(B, M, N, seed=31, D=D)
+    # row (1, 7): scores q.k = -(D/64) * 32 <= -32 for every key (K entries 0.5, Q -1)
+    k = k.copy()
+    k[1] = np.float16(0.5)
+    q = q.copy()
+    q[1, 7] = np.float16(-1.0)
+    out = run_gpu(q, k, v, gpu, splits=splits)
+    assert np.isnan(out[1, 7]).all(), "all-underflow row is not NaN"
+    keep = np.ones((B, M), dtype=bool)
+    keep[1, 7] = False
+    assert np.isfinite(out[keep]).all()
+    ref = oracle.gqa_f64(q, k, v)
+    err = np.abs(out.astype(np.float64) - ref)[keep]
+    assert (err <= CONTRACT_ATOL + CONTRACT_RTOL * np.abs(ref[keep])).all()
