@@ -60,6 +60,10 @@ def parse_args():
     ap.add_argument("--qk-norm", action="store_true",
                     help="time the QK-normalised variant (rms_norm of Q rows and key vectors, "
                          "eps 1e-6) instead of the plain graph")
+    ap.add_argument("--boundary", action="store_true",
+                    help="time the forward's pieces instead: the partial kernel alone, followed by a "
+                         "one-block fill kernel, followed by the combine, and followed by the combine "
+                         "reading partials written earlier (one JSON line)")
     ap.add_argument("--sweep-splits", default="",
                     help="comma-separated split counts: time the forward at each (same inputs, "
                          "graph replay) and print one JSON line per count instead of the bench line")
@@ -319,6 +323,40 @@ def main():
                               "rotating_sets": R, "steps": max(1, math.ceil(args.steps / gsteps)) * gsteps}),
                   flush=True)
             del ws_sp
+        return
+
+    if args.boundary and not args.qk_norm and eff > 1:
+        # What the second launch costs in the forward: a fill kernel of one
+        # workgroup in the combine's place (the kernel boundary alone), the
+        # combine itself, and the combine reading partials that an earlier
+        # call wrote (not the ones the partial kernel just wrote).
+        tiny = torch.zeros(64, device=dev)
+        ws_old = mga.workspace_for(B, M, N, D, splits, device=dev)
+        old_ptr = ws_old.data_ptr()
+        rc = lib.mga_gqa_partial(*ptrs[0], optr[0], B, M, N, D, splits, old_ptr, ws_bytes, sh)
+        if rc:
+            raise mga.GqaError(rc)
+
+        def comb_ws(i, wp):
+            rc = lib.mga_gqa_combine(optr[i % R], B, M, N, D, splits, wp, ws_bytes, sh)
+            if rc:
+                raise mga.GqaError(rc)
+
+        pieces = {
+            "partial": lambda i: partial(i),
+            "partial_then_fill": lambda i: (partial(i), tiny.zero_()),
+            "forward": lambda i: fwd(i),
+            "partial_then_combine_of_older_partials": lambda i: (partial(i), comb_ws(i, old_ptr)),
+            "fill_alone": lambda i: tiny.zero_(),
+            "combine_alone": lambda i: comb_ws(i, ws_ptr),
+        }
+        out = {"workload": cfg.name, "splits": eff, "rotating_sets": R,
+               "timing": "hip-graph replay, events on the launch stream, us per call"}
+        with torch.cuda.stream(stream):
+            for name, fn in pieces.items():
+                ms, _, _ = time_graph(torch, stream, fn, args.steps, gsteps, args.warmup)
+                out[name + "_us"] = round(ms * 1e3, 3)
+        print(json.dumps(out), flush=True)
         return
 
     print(f"[bench] {cfg.name} B={B} M={M} N={N} D={D} splits={eff} rotating sets={R} "
