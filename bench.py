@@ -325,7 +325,11 @@ def main():
             del ws_sp
         return
 
-    if args.boundary and not args.qk_norm and eff > 1:
+    if args.boundary and (args.qk_norm or eff == 1):
+        print("--boundary times the plain forward's combine launch: it needs a split plan "
+              f"(this one has {eff} split{'s' if eff > 1 else ''}) and no --qk-norm", file=sys.stderr)
+        sys.exit(2)
+    if args.boundary:
         # What the second launch costs in the forward: a fill kernel of one
         # workgroup in the combine's place (the kernel boundary alone), the
         # combine itself, and the combine reading partials that an earlier
