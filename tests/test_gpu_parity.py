@@ -119,6 +119,48 @@ def test_small_and_ragged_shapes_all_splits(gpu, B, M, N, D):
         assert_parity(run_gpu(q, k, v, gpu, splits=s), ref, q, k, v, f"B{B} M{M} N{N} D{D} s{s}")
 
 
+def _random_cases(n, seed):
+    """Seeded shapes, both head dims, any N (contiguous K repacked when
+    N % 8 != 0), splits 0 (policy) or 1..blocks, in three kinds: few batch
+    rows (B up to 6, N up to 5000: 32-row tiles, long key streams); many (B
+    up to 280, B*M*N up to 8M: the 128- and 256-row tiles on short key
+    ranges); and between (B 8-40, M 129-300, N from 1024: 64-row tiles over
+    split key ranges)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        if i % 3 == 0:
+            B = int(rng.integers(1, 7))
+            M = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 129)),
+                                int(rng.integers(129, 301))]))
+            N = int(rng.integers(1, 5001))
+        elif i % 3 == 1:
+            D = 64  # the 128- and 256-row tiles exist at D = 64
+            B = int(rng.integers(8, 281))
+            M = int(rng.integers(33, 301))
+            N = int(rng.integers(1, max(2, min(700, 8_000_000 // (B * M)))))
+        else:  # 64-row tiles over split key ranges (the shared ring)
+            D = 64
+            B = int(rng.integers(16, 41))
+            M = int(rng.integers(129, 301))
+            N = int(rng.integers(2048, max(2049, min(3000, 8_000_000 // (B * M)))))
+        blocks = -(-N // 128)
+        s = 0 if rng.random() < 0.5 else int(rng.integers(1, blocks + 1))
+        cases.append((B, M, N, D, s))
+    return cases
+
+
+@pytest.mark.parametrize("B,M,N,D,splits", _random_cases(42, 2027))
+def test_random_shapes_against_oracle(gpu, B, M, N, D, splits):
+    q, k, v = make_qkv(B, M, N, seed=B * 100003 + M * 1009 + N * 7 + D + splits, D=D)
+    _say(f"[random] B={B} M={M} N={N} D={D} splits={splits} "
+         f"(effective {mga.mga_gqa_effective_splits(B, M, N, D, splits)}, "
+         f"rows {mga.mga_gqa_plan(B, M, N, D, splits)[1]})")
+    assert_parity(run_gpu(q, k, v, gpu, splits=splits), oracle.gqa_f64(q, k, v), q, k, v,
+                  f"B{B} M{M} N{N} D{D} s{splits}")
+
+
 def _quantized(shape, seed, scale):
     """Seeded uniform inputs on a 1/256 grid (exact in fp16), cheap to draw in bulk."""
     rng = np.random.Generator(np.random.PCG64(seed))
