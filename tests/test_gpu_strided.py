@@ -188,3 +188,47 @@ def test_contiguous_k_with_unaligned_rows_is_repacked(gpu, N, D):
     o2 = mga.gqa_forward(tq, kview, tv, qk_norm=True)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
+
+
+def _random_views(n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(n):
+        D = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 9))
+        M = int(rng.integers(1, 300))
+        N = int(rng.integers(1, 3000))
+        blocks = -(-N // mga.KEY_BLOCK)
+        s = 0 if rng.random() < 0.5 else int(rng.integers(1, blocks + 1))
+        pads = tuple(int(8 * rng.integers(0, 5)) for _ in range(5))  # q row, q batch rows, k, v row, o row
+        km = bool(rng.random() < 0.5)
+        out.append((B, M, N, D, s, km, pads))
+    return out
+
+
+@pytest.mark.parametrize("B,M,N,D,splits,key_major,pads", _random_views(24, 4242))
+def test_random_strided_views_equal_contiguous(gpu, B, M, N, D, splits, key_major, pads):
+    """Seeded shapes with every operand a strided view (Q and O inside wider
+    rows, Q's batches further apart, K key-major from a longer cache or in
+    padded head-dim-major rows, V inside wider rows), the memory outside the
+    views NaN (inputs) or a sentinel (output): the result equals the
+    contiguous path's bit for bit and nothing outside O's view is written."""
+    import torch
+    qpad, qrows, kpad, vpad, opad = pads
+    q, k, v = make_qkv(B, M, N, seed=B * 7919 + M * 31 + N + D + splits, D=D)
+    ref = _run(_t(q, gpu), _t(k, gpu), _t(v, gpu), splits)
+    qb = torch.full((B, M + qrows, D + qpad), float("nan"), dtype=torch.float16, device=gpu)
+    qb[:, :M, :D] = _t(q, gpu)
+    qv = qb[:, :M, :D]
+    kv = _key_major(k, gpu, capacity=N + kpad) if key_major else _padded_rows(k, gpu, kpad)
+    vb = torch.full((B, N, D + vpad), float("nan"), dtype=torch.float16, device=gpu)
+    vb[:, :, :D] = _t(v, gpu)
+    vv = vb[:, :, :D]
+    ob = torch.full((B, M, D + opad), 7.0, dtype=torch.float16, device=gpu)
+    ov = ob[:, :, :D]
+    _say(f"[random views] B={B} M={M} N={N} D={D} splits={splits} K {'key-major' if key_major else 'rows'} "
+         f"q{tuple(qv.stride())} k{tuple(kv.stride())} v{tuple(vv.stride())} o{tuple(ov.stride())}")
+    _run(qv, kv, vv, splits, out=ov)
+    assert torch.equal(ov, ref), "strided views differ from the contiguous path"
+    if opad:
+        assert (ob[:, :, D:] == 7.0).all(), "a write outside O's view"
