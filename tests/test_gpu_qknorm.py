@@ -171,3 +171,35 @@ def test_qknorm_deterministic_and_split_consistent(gpu):
     for s, o in outs.items():
         assert np.max(np.abs(o - outs[1])) <= 2e-3, s
     _check(outs[4].astype(np.float16), q, k, v, "qknorm s4", 4)
+
+
+def _random_qkn_cases(n, seed):
+    """Seeded shapes for the QK-normalised path: few batch rows with long key
+    ranges (M up to 32: 32-row tiles; more: 64-row tiles), and more batch
+    rows with shorter ones (64-row tiles, on the shared ring once the keys
+    are split), both head dims (D = 128: 32-row tiles), any N, policy or
+    random splits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        if i % 2 == 0:
+            M = int(rng.integers(1, 33)) if rng.random() < 0.5 else int(rng.integers(33, 300))
+            B, N = int(rng.integers(1, 5)), int(rng.integers(1, 5000))
+        else:
+            B, M = int(rng.integers(8, 33)), int(rng.integers(65, 300))
+            N = int(rng.integers(512, max(513, min(3000, 6_000_000 // (B * M)))))
+        blocks = -(-N // mga.KEY_BLOCK)
+        s = 0 if rng.random() < 0.5 else int(rng.integers(1, blocks + 1))
+        cases.append((B, M, N, D, s))
+    return cases
+
+
+@pytest.mark.parametrize("B,M,N,D,splits", _random_qkn_cases(24, 5150))
+def test_qknorm_random_shapes(gpu, B, M, N, D, splits):
+    q, k, v = make_qkv(B, M, N, seed=B * 6007 + M * 17 + N + D + splits, qk_std=1.0, D=D)
+    q, k = _rescaled(q, k, B + M + N)
+    _say(f"[qknorm random] B={B} M={M} N={N} D={D} splits={splits} "
+         f"plan={mga.mga_gqa_qknorm_plan(B, M, N, D, splits)}")
+    _check(_run(q, k, v, gpu, splits), q, k, v, f"qknorm B{B} M{M} N{N} D{D} s{splits}",
+           _eff(q, k, splits))
