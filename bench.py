@@ -151,11 +151,13 @@ def gpu_clocks():
     return out or None
 
 
-def read_load_clock(config: str):
+def read_load_clock(config: str, qk_norm: bool = False):
     """Shader clock under load (GHz) from the committed counter pass of this
-    workload: GRBM_GUI_ACTIVE per XCD over the dispatch's own duration, if that
-    pass was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"counters_gqa_partial_{config.replace('gqa_', '')}.md")
+    workload (and path): SQ_BUSY_CYCLES per shader engine over the dispatch's
+    own duration, if that pass was taken on the current kernel source; else
+    None."""
+    tag = ("qknorm_" if qk_norm else "") + config.replace("gqa_", "")
+    path = os.path.join(ROOT, "profiles", f"counters_gqa_partial_{tag}.md")
     try:
         text = open(path).read()
     except OSError:
@@ -429,7 +431,7 @@ def main():
     else:
         achieved, peak, unit = flops / sp / 1e12, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"
         achieved_f = flops / s / 1e12
-    load_ghz = read_load_clock(cfg.name)
+    load_ghz = read_load_clock(cfg.name, args.qk_norm)
 
     result = {
         "metric": "fused GQA exp-sum-div attention TFLOP/s + HBM GB/s on 1 MI355X",

@@ -79,3 +79,8 @@ def test_load_clock_only_from_the_current_source(tmp_path, monkeypatch):
     f.write_text("kernel_source_sha256: " + "0" * 64 + "\nload_clock_ghz: 2.05\n")
     assert bench.read_load_clock("gqa_b16_m256_n4096") is None
     assert bench.read_load_clock("gqa_b64_m8_n8192") is None
+    # the QK-normalised path reads its own pass
+    g = d / "counters_gqa_partial_qknorm_b16_m256_n4096.md"
+    g.write_text(f"kernel_source_sha256: {bench.kernel_source_sha()}\nload_clock_ghz: 1.89\n")
+    assert bench.read_load_clock("gqa_b16_m256_n4096", qk_norm=True) == 1.89
+    assert bench.read_load_clock("gqa_b16_m256_n4096") is None
